@@ -161,6 +161,17 @@ def backward_head(setting: int, q1, k1, q2, k2, scale: float, causal: bool, dkl=
     return dq, dk
 
 
+def dlogits_head(setting: int, q1, k1, q2, k2, scale: float, causal: bool, dkl=None):
+    """dL/dS of the chosen setting for one head, fp64 [N_Q, N_K] (masked entries 0)."""
+    q1, k1, q2, k2 = map(_as64, (q1, k1, q2, k2))
+    n_q = q1.shape[0]
+    g = np.ones(n_q) if dkl is None else _as64(dkl)
+    rows = np.arange(n_q)
+    mask, lp1, _, lp2, _ = _row_block_state(q1, k1, q2, k2, scale, causal, rows)
+    kl = _kl_of_rows(mask, lp1, lp2)
+    return _dlogits(setting, mask, lp1, lp2, kl, g)
+
+
 def dq_rows(setting: int, q1, k1, q2, k2, scale: float, causal: bool, rows, dkl=None):
     """dQ (of the chosen setting) for selected query rows only; exact per row."""
     q1, k1, q2, k2 = map(_as64, (q1, k1, q2, k2))

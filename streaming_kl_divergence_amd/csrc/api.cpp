@@ -1,0 +1,247 @@
+// C ABI of the attention-KL library: argument validation, workspace sizing,
+// kernel choice and launches.  The operations are defined in streamkl.h; the
+// kernels live in fwd.hip and bwd.hip.
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "kernels.hpp"
+#include "streamkl.h"
+
+namespace {
+
+constexpr int kMaxSplits = 1024;
+
+int device_cus() {
+  // Compute units of the current device (cached per device id, 64 devices).
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_common(const void* q1, const void* k1, const void* q2, const void* k2, int n_q, int n_k,
+                 int heads, int head_dim, int causal, float scale, int dtype) {
+  if (!q1 || !k1 || !q2 || !k2) return STREAMKL_ERR_NULL;
+  if (n_q < 1 || n_k < 1 || heads < 1) return STREAMKL_ERR_SHAPE;
+  if ((long long)heads * n_q >= (1LL << 31) || (long long)heads * n_k >= (1LL << 31)) return STREAMKL_ERR_SHAPE;
+  if (causal && n_q > n_k) return STREAMKL_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return STREAMKL_ERR_UNSUPPORTED;
+  if (dtype != STREAMKL_BF16 && dtype != STREAMKL_FP32) return STREAMKL_ERR_UNSUPPORTED;
+  if (!isfinite(scale) || scale < 0.f) return STREAMKL_ERR_SCALE;
+  if (!aligned16(q1) || !aligned16(k1) || !aligned16(q2) || !aligned16(k2)) return STREAMKL_ERR_ALIGN;
+  return STREAMKL_OK;
+}
+
+skl::FwdParams fwd_params(const void* q1, const void* k1, const void* q2, const void* k2, int n_q, int n_k,
+                          int heads, int causal, float scale, float* kl, float* lse1, float* lse2) {
+  skl::FwdParams p;
+  memset(&p, 0, sizeof(p));
+  p.q1 = (const char*)q1;
+  p.k1 = (const char*)k1;
+  p.q2 = (const char*)q2;
+  p.k2 = (const char*)k2;
+  p.n_q = n_q;
+  p.n_k = n_k;
+  p.heads = heads;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  p.c = scale * 1.4426950408889634f;
+  p.kl = kl;
+  p.lse1 = lse1;
+  p.lse2 = lse2;
+  p.splits = 1;
+  p.split_keys = n_k;
+  return p;
+}
+
+// keys per split for `splits` ranges, rounded up to whole key tiles
+int split_keys_for(int n_k, int splits) {
+  const int t = skl::kFwdKeyTile;
+  const int tiles = (n_k + t - 1) / t;
+  const int per = (tiles + splits - 1) / splits;
+  return per * t;
+}
+
+// number of non-empty ranges once rounded to whole tiles
+int effective_splits(int n_k, int splits) {
+  const int keys = split_keys_for(n_k, splits);
+  return (n_k + keys - 1) / keys;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? STREAMKL_OK : STREAMKL_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int streamkl_splitk_auto(int n_q, int n_k, int heads, int head_dim) {
+  (void)head_dim;
+  if (n_q < 1 || n_k < 1 || heads < 1) return 1;
+  const int nw = skl::fwd_waves(n_q);
+  const long long blocks = (long long)heads * ((n_q + skl::fwd_queries_per_block(nw) - 1) /
+                                               skl::fwd_queries_per_block(nw));
+  // aim for about 8 workgroups per compute unit, each streaming >= 8 key tiles
+  const long long want = 8LL * device_cus();
+  long long s = (want + blocks - 1) / blocks;
+  const long long max_by_len = (n_k + 8 * skl::kFwdKeyTile - 1) / (8 * skl::kFwdKeyTile);
+  if (s > max_by_len) s = max_by_len;
+  if (s < 1) s = 1;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return effective_splits(n_k, (int)s);
+}
+
+size_t streamkl_workspace_bytes(int op, int n_q, int n_k, int heads, int head_dim, int num_splits,
+                                streamkl_bwd_path path) {
+  if (n_q < 1 || n_k < 1 || heads < 1 || (head_dim != 64 && head_dim != 128)) return (size_t)-1;
+  if (op == 0) {
+    if (num_splits < 0 || num_splits > kMaxSplits) return (size_t)-1;
+    const int s = num_splits == 0 ? streamkl_splitk_auto(n_q, n_k, heads, head_dim)
+                                  : effective_splits(n_k, num_splits);
+    return (size_t)s * heads * n_q * 5 * sizeof(float);
+  }
+  if (op == 1 || op == 2) {
+    if (path != STREAMKL_BWD_AUTO && path != STREAMKL_BWD_FUSED && path != STREAMKL_BWD_SEPARATE)
+      return (size_t)-1;
+    return 0;
+  }
+  return (size_t)-1;
+}
+
+int streamkl_fwd(const void* q1, const void* k1, const void* q2, const void* k2, int n_q, int n_k,
+                 int heads, int head_dim, int causal, float scale, streamkl_dtype dtype, float* kl,
+                 float* lse1, float* lse2, hipStream_t stream) {
+  int st = check_common(q1, k1, q2, k2, n_q, n_k, heads, head_dim, causal, scale, (int)dtype);
+  if (st) return st;
+  if (!kl || !lse1 || !lse2) return STREAMKL_ERR_NULL;
+  skl::FwdParams p = fwd_params(q1, k1, q2, k2, n_q, n_k, heads, causal, scale, kl, lse1, lse2);
+  return status_of(skl::launch_fwd(p, (int)dtype, head_dim, skl::fwd_waves(n_q), false, stream));
+}
+
+int streamkl_fwd_splitk(const void* q1, const void* k1, const void* q2, const void* k2, int n_q, int n_k,
+                        int heads, int head_dim, int causal, float scale, streamkl_dtype dtype,
+                        int num_splits, float* kl, float* lse1, float* lse2, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  int st = check_common(q1, k1, q2, k2, n_q, n_k, heads, head_dim, causal, scale, (int)dtype);
+  if (st) return st;
+  if (!kl || !lse1 || !lse2) return STREAMKL_ERR_NULL;
+  if (num_splits < 0 || num_splits > kMaxSplits) return STREAMKL_ERR_UNSUPPORTED;
+  const int splits = num_splits == 0 ? streamkl_splitk_auto(n_q, n_k, heads, head_dim)
+                                     : effective_splits(n_k, num_splits);
+  const size_t need = (size_t)splits * heads * n_q * 5 * sizeof(float);
+  if (!workspace || workspace_bytes < need) return STREAMKL_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return STREAMKL_ERR_ALIGN;
+  skl::FwdParams p = fwd_params(q1, k1, q2, k2, n_q, n_k, heads, causal, scale, kl, lse1, lse2);
+  p.part = (float*)workspace;
+  p.splits = splits;
+  p.split_keys = split_keys_for(n_k, splits);
+  hipError_t e = skl::launch_fwd(p, (int)dtype, head_dim, skl::fwd_waves(n_q), true, stream);
+  if (e != hipSuccess) return STREAMKL_ERR_HIP;
+  return status_of(skl::launch_splitk_combine(p, stream));
+}
+
+int streamkl_bwd_select(int n_q, int n_k, int heads, int head_dim, int causal) {
+  (void)n_k;
+  (void)causal;
+  // The fused kernel adds every workgroup's dQ tile into dQ with fp32
+  // atomics.  It wins only while that buffer is small enough to stay in the
+  // on-chip caches; otherwise the separate dK and dQ kernels are used.
+  const double dq_bytes = (double)heads * n_q * head_dim * 4.0;
+  return dq_bytes <= 16.0 * 1024 * 1024 ? STREAMKL_BWD_FUSED : STREAMKL_BWD_SEPARATE;
+}
+
+// Key ranges for the separate path's dQ kernel: enough workgroups to fill the
+// chip when there are few query blocks (each range adds into dQ atomically).
+static int dq_splits_for(int n_q, int n_k, int heads) {
+  const long long blocks = (long long)heads * ((n_q + skl::kBwdQueriesPerBlock - 1) / skl::kBwdQueriesPerBlock);
+  const long long want = 4LL * device_cus();
+  if (blocks >= want) return 1;
+  long long s = (want + blocks - 1) / blocks;
+  const long long max_by_len = (n_k + 1023) / 1024;   // at least ~16 key tiles per range
+  if (s > max_by_len) s = max_by_len;
+  if (s > 64) s = 64;
+  return s < 1 ? 1 : (int)s;
+}
+
+static int bwd_common(int setting, const void* q1, const void* k1, const void* q2, const void* k2, int n_q,
+                      int n_k, int heads, int head_dim, int causal, float scale, streamkl_dtype dtype,
+                      const float* lse1, const float* lse2, const float* kl, const float* dkl, float* dq,
+                      float* dk, streamkl_bwd_path path, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  int st = check_common(q1, k1, q2, k2, n_q, n_k, heads, head_dim, causal, scale, (int)dtype);
+  if (st) return st;
+  if (!lse1 || !lse2 || !dq || !dk || (setting == 2 && !kl)) return STREAMKL_ERR_NULL;
+  if (path != STREAMKL_BWD_AUTO && path != STREAMKL_BWD_FUSED && path != STREAMKL_BWD_SEPARATE)
+    return STREAMKL_ERR_UNSUPPORTED;
+  if (!aligned16(dq) || !aligned16(dk)) return STREAMKL_ERR_ALIGN;
+  if (path == STREAMKL_BWD_AUTO) {
+    path = (streamkl_bwd_path)streamkl_bwd_select(n_q, n_k, heads, head_dim, causal);
+    if (path == STREAMKL_BWD_FUSED && !skl::fused_supported((int)dtype, head_dim)) path = STREAMKL_BWD_SEPARATE;
+  }
+  if (path == STREAMKL_BWD_FUSED && !skl::fused_supported((int)dtype, head_dim)) return STREAMKL_ERR_UNSUPPORTED;
+  skl::BwdParams p;
+  memset(&p, 0, sizeof(p));
+  p.q1 = (const char*)q1;
+  p.k1 = (const char*)k1;
+  p.q2 = (const char*)q2;
+  p.k2 = (const char*)k2;
+  p.n_q = n_q;
+  p.n_k = n_k;
+  p.heads = heads;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  p.c = scale * 1.4426950408889634f;
+  p.lse1 = lse1;
+  p.lse2 = lse2;
+  p.kl = kl;
+  p.dkl = dkl;
+  p.dq = dq;
+  p.dk = dk;
+  p.setting = setting;
+  p.dq_splits = path == STREAMKL_BWD_SEPARATE ? dq_splits_for(n_q, n_k, heads) : 1;
+  if (path == STREAMKL_BWD_FUSED) return status_of(skl::launch_bwd_fused(p, (int)dtype, head_dim, stream));
+  return status_of(skl::launch_bwd_separate(p, (int)dtype, head_dim, stream));
+}
+
+int streamkl_bwd_set1(const void* q1, const void* k1, const void* q2, const void* k2, int n_q, int n_k,
+                      int heads, int head_dim, int causal, float scale, streamkl_dtype dtype,
+                      const float* lse1, const float* lse2, const float* dkl, float* dq2, float* dk2,
+                      streamkl_bwd_path path, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_common(1, q1, k1, q2, k2, n_q, n_k, heads, head_dim, causal, scale, dtype, lse1, lse2, nullptr,
+                    dkl, dq2, dk2, path, workspace, workspace_bytes, stream);
+}
+
+int streamkl_bwd_set2(const void* q1, const void* k1, const void* q2, const void* k2, int n_q, int n_k,
+                      int heads, int head_dim, int causal, float scale, streamkl_dtype dtype,
+                      const float* lse1, const float* lse2, const float* kl, const float* dkl, float* dq1,
+                      float* dk1, streamkl_bwd_path path, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  return bwd_common(2, q1, k1, q2, k2, n_q, n_k, heads, head_dim, causal, scale, dtype, lse1, lse2, kl, dkl,
+                    dq1, dk1, path, workspace, workspace_bytes, stream);
+}
+
+const char* streamkl_strerror(int status) {
+  switch (status) {
+    case STREAMKL_OK: return "ok";
+    case STREAMKL_ERR_NULL: return "a required pointer is NULL";
+    case STREAMKL_ERR_SHAPE: return "invalid shape (n_q, n_k, heads < 1, too large, or causal with n_q > n_k)";
+    case STREAMKL_ERR_UNSUPPORTED: return "unsupported head_dim, dtype, path or split count";
+    case STREAMKL_ERR_SCALE: return "scale must be finite and >= 0";
+    case STREAMKL_ERR_WORKSPACE: return "workspace missing or too small";
+    case STREAMKL_ERR_HIP: return "HIP launch error";
+    case STREAMKL_ERR_ALIGN: return "array not 16-byte aligned";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

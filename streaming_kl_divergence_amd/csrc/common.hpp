@@ -1,0 +1,106 @@
+// Shared device helpers for the attention-KL kernels on gfx950 (CDNA4).
+//
+// Tiles of K (or Q) rows live in LDS as rows of 16-byte chunks.  A chunk's
+// slot inside its row is XOR-swizzled with the low bits of the row index, so
+// that the 32-row MFMA operand reads (one 16-byte chunk per lane, 16 lanes per
+// LDS cycle) hit 16 distinct chunk slots and never conflict on a bank.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace skl {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define SKL_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Running maxima start here instead of -inf: finite, so (m_old - m_new) * c
+// stays a number even when the scale (and so c) is zero.
+constexpr float kMaxInit = -1.0e30f;
+
+// Row geometry of a [rows, D] tile of element type T.
+template <typename T, int D>
+struct Geom {
+  static constexpr int kRowBytes = D * (int)sizeof(T);
+  static constexpr int kChunks = kRowBytes / 16;          // 16-byte chunks per row
+  static constexpr int kGroups = kChunks / 2;             // chunk pairs (one per lane half)
+  static constexpr int kSwz = (kChunks < 16 ? kChunks : 16) - 1;
+  static_assert(kChunks >= 8, "rows must be at least 128 bytes");
+};
+
+// Byte offset of chunk `c` of tile row `row` inside an LDS tile.
+template <typename T, int D>
+__device__ __forceinline__ int lds_chunk_off(int row, int c) {
+  using G = Geom<T, D>;
+  return (row * G::kChunks + (c ^ (row & G::kSwz))) * 16;
+}
+
+// acc(32 x 32) += A(32 x k) B(k x 32) for one chunk pair.  Lane l supplies one
+// 16-byte chunk of row (l % 32) of A and of column (l % 32) of B; lanes l and
+// l + 32 hold the two chunks of the pair.  Any fixed assignment of a row's
+// elements to k works as long as A and B use the same one, so chunks can be
+// read straight from row-major memory.
+//   bf16: one v_mfma_f32_32x32x16_bf16 (8 elements per lane);
+//   fp32: four v_mfma_f32_32x32x2_f32  (1 element per lane each).
+// Result layout (both): lane l, register r holds row 8*(r/4) + 4*(l/32) + r%4,
+// column l % 32.
+template <typename T>
+__device__ __forceinline__ f32x16 mfma_chunk(u32x4 a, u32x4 b, f32x16 acc);
+
+template <>
+__device__ __forceinline__ f32x16 mfma_chunk<__bf16>(u32x4 a, u32x4 b, f32x16 acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ f32x16 mfma_chunk<float>(u32x4 a, u32x4 b, f32x16 acc) {
+  const f32x4 fa = __builtin_bit_cast(f32x4, a);
+  const f32x4 fb = __builtin_bit_cast(f32x4, b);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa.x, fb.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa.y, fb.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa.z, fb.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa.w, fb.w, acc, 0, 0, 0);
+  return acc;
+}
+
+// Row index (within a 32 x 32 MFMA result block) of register r in lane half h.
+__device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Issue the asynchronous copy of a [BK, D] tile (rows key0 .. key0+BK-1 of the
+// head whose row 0 is at `g`) into LDS with the swizzled layout.  Rows past
+// n_rows are clamped to the last row, so every load is in bounds; the caller
+// masks those rows out.  Every lane of all NW waves takes part.
+template <typename T, int D, int BK, int NW>
+__device__ __forceinline__ void issue_tile_async(const char* __restrict__ g, int key0, int n_rows,
+                                                 SKL_LDS char* tile, int tid, int wave) {
+  using G = Geom<T, D>;
+  constexpr int kSlots = BK * G::kChunks;
+  static_assert(kSlots % (NW * 64) == 0, "tile must split evenly over the workgroup");
+  constexpr int kPer = kSlots / (NW * 64);
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int slot = i * NW * 64 + tid;
+    const int row = slot / G::kChunks;
+    const int pc = slot % G::kChunks;
+    const int c = pc ^ (row & G::kSwz);
+    const int src_row = min(key0 + row, n_rows - 1);
+    const char* src = g + (size_t)src_row * G::kRowBytes + c * 16;
+    // lane i of this wave lands at base + 16 * i
+    __builtin_amdgcn_global_load_lds((const void*)src,
+                                     (SKL_LDS void*)(tile + (i * NW * 64 + wave * 64) * 16), 16, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void wait_async_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+}  // namespace skl

@@ -1,0 +1,273 @@
+// Fused one-pass forward of the attention KL divergence, and its split-K form.
+//
+// "StreamKL: Fast and Memory-Efficient KL Divergence for Boosting Attention
+// Distillation" (gist.science technical summary):
+//   Methodology 1, Online Formulation - five running scalars per row
+//     (maxima m1, m2; exp-sums l1, l2; acc, the P1-weighted logit
+//     difference), one pass over key tiles, row loss acc/l1 + LSE2 - LSE1,
+//     LSE_t = m_t + log l_t; acc is one value per row (not a B_Q x d block),
+//     so each tile rescales it once; causal key tiles past the frontier are
+//     never loaded.
+//   Methodology 3, Split-K Variant - for few queries the key range is cut
+//     into pieces handled by different workgroups, whose partial states are
+//     merged afterwards.
+//
+// gfx950 mapping
+//   * Workgroup = NW waves; each wave owns 32 query rows of one head.  Its Q1
+//     and Q2 rows stay in VGPRs for the whole pass (the B operand).
+//   * K1 and K2 tiles of 64 keys stream through double-buffered LDS, copied
+//     with global_load_lds_dwordx4 (no VGPR staging) in a swizzled layout.
+//   * The MFMA computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so each
+//     lane holds one query and 16 of every 32 keys.  A lane keeps its own
+//     five-scalar state for its half of the keys; the two halves are merged
+//     once at the end (the same merge as split-K), so the tile loop has no
+//     cross-lane reductions.
+//   * Scores stay in raw units; exp2 takes fma(S, c, -m*c) with
+//     c = scale*log2(e); acc is kept in raw units and scaled once at the end.
+//   * Causal: Q blocks are launched heaviest first; tiles past a wave's
+//     frontier are skipped; only tiles that cross the diagonal or the end of
+//     the key range take the masked code path.
+//   * Workgroup ids map head-fastest, so all blocks of one head go to the
+//     same XCD (blocks are dealt round-robin over the 8 XCDs) and share its
+//     L2 for the K stream.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace skl {
+
+template <typename T, int D, int NW, bool SPLIT>
+__global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
+  using G = Geom<T, D>;
+  constexpr int BK = kFwdKeyTile;
+  constexpr int BQ = 32 * NW;
+  constexpr int NKB = BK / 32;
+  constexpr int TILE = BK * G::kRowBytes;
+  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * TILE];  // [buffer][K1, K2]
+  SKL_LDS char* lds = (SKL_LDS char*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5;
+  const int col = lane & 31;
+
+  const int nqb = (p.n_q + BQ - 1) / BQ;
+  int bid = blockIdx.x;
+  const int head = bid % p.heads;
+  bid /= p.heads;
+  int split = 0;
+  if (SPLIT) {
+    split = bid % p.splits;
+    bid /= p.splits;
+  }
+  const int qb = p.causal ? (nqb - 1 - bid) : bid;
+
+  const int off = p.n_k - p.n_q;
+  const int q0 = qb * BQ;
+  const int qw0 = q0 + wave * 32;
+  const int qrow = qw0 + col;
+
+  // key range of this workgroup: [kbeg, klimit), cut at the causal frontier
+  int kbeg = 0, klimit = p.n_k;
+  if (SPLIT) {
+    kbeg = split * p.split_keys;
+    klimit = min(p.n_k, kbeg + p.split_keys);
+  }
+  int kend = klimit;
+  if (p.causal) kend = min(kend, min(q0 + BQ, p.n_q) + off);
+  const int ntiles = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+
+  const size_t hq = (size_t)head * p.n_q;
+  const size_t hk = (size_t)head * p.n_k;
+  const char* k1 = p.k1 + hk * G::kRowBytes;
+  const char* k2 = p.k2 + hk * G::kRowBytes;
+
+  // this lane's query row: the chunks 2g + h of Q1 and Q2
+  u32x4 qf1[G::kGroups], qf2[G::kGroups];
+  {
+    const int qr = min(qrow, p.n_q - 1);
+    const char* a1 = p.q1 + (hq + qr) * G::kRowBytes + h * 16;
+    const char* a2 = p.q2 + (hq + qr) * G::kRowBytes + h * 16;
+#pragma unroll
+    for (int g = 0; g < G::kGroups; ++g) {
+      qf1[g] = *(const u32x4*)(a1 + g * 32);
+      qf2[g] = *(const u32x4*)(a2 + g * 32);
+    }
+  }
+
+  float m1 = kMaxInit, m2 = kMaxInit, l1 = 0.f, l2 = 0.f, acc = 0.f;
+  const float c = p.c;
+  // the wave's last real query; waves past n_q have nothing to compute
+  const int wlast = min(qw0 + 31, p.n_q - 1);
+  const bool wave_idle = qw0 >= p.n_q;
+
+  if (ntiles > 0) {
+    issue_tile_async<T, D, BK, NW>(k1, kbeg, p.n_k, lds, tid, wave);
+    issue_tile_async<T, D, BK, NW>(k2, kbeg, p.n_k, lds + TILE, tid, wave);
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    wait_async_loads();
+    __syncthreads();  // tile t visible to all waves; buffer t+1 free again
+    const int buf = t & 1;
+    if (t + 1 < ntiles) {
+      SKL_LDS char* nb = lds + (buf ^ 1) * 2 * TILE;
+      issue_tile_async<T, D, BK, NW>(k1, kbeg + (t + 1) * BK, p.n_k, nb, tid, wave);
+      issue_tile_async<T, D, BK, NW>(k2, kbeg + (t + 1) * BK, p.n_k, nb + TILE, tid, wave);
+    }
+    const int k0 = kbeg + t * BK;
+    if (wave_idle || (p.causal && k0 > wlast + off)) continue;  // wave-uniform
+
+    const SKL_LDS char* t1 = lds + buf * 2 * TILE;
+    const SKL_LDS char* t2 = t1 + TILE;
+    f32x16 s1[NKB], s2[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      s1[kb] = f32x16{};
+      s2[kb] = f32x16{};
+#pragma unroll
+      for (int g = 0; g < G::kGroups; ++g) {
+        const int off_b = lds_chunk_off<T, D>(kb * 32 + col, 2 * g + h);
+        const u32x4 a1 = *(const SKL_LDS u32x4*)(t1 + off_b);
+        const u32x4 a2 = *(const SKL_LDS u32x4*)(t2 + off_b);
+        s1[kb] = mfma_chunk<T>(a1, qf1[g], s1[kb]);
+        s2[kb] = mfma_chunk<T>(a2, qf2[g], s2[kb]);
+      }
+    }
+
+    const bool need_mask = (k0 + BK > klimit) || (p.causal && k0 + BK - 1 > qw0 + off);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + kb * 32 + acc_row(r, h);
+          const bool ok = key < klimit && (!p.causal || key <= qrow + off);
+          if (!ok) {
+            s1[kb][r] = -INFINITY;
+            s2[kb][r] = -INFINITY;
+          }
+        }
+    }
+    float tm1 = -INFINITY, tm2 = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        tm1 = fmaxf(tm1, s1[kb][r]);
+        tm2 = fmaxf(tm2, s2[kb][r]);
+      }
+    const float n1 = fmaxf(m1, tm1), n2 = fmaxf(m2, tm2);
+    const float a1 = fast_exp2((m1 - n1) * c), a2 = fast_exp2((m2 - n2) * c);
+    m1 = n1;
+    m2 = n2;
+    const float mc1 = n1 * c, mc2 = n2 * c;
+    float sl1[4] = {0.f, 0.f, 0.f, 0.f}, sl2[4] = {0.f, 0.f, 0.f, 0.f}, sa[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float x1 = s1[kb][r], x2 = s2[kb][r];
+        float e1 = fast_exp2(fmaf(x1, c, -mc1));
+        float e2 = fast_exp2(fmaf(x2, c, -mc2));
+        float d = x1 - x2;
+        if (need_mask) {
+          const bool ok = x1 != -INFINITY;  // real scores are finite
+          e1 = ok ? e1 : 0.f;
+          e2 = ok ? e2 : 0.f;
+          d = ok ? d : 0.f;
+        }
+        const int j = r & 3;
+        sl1[j] += e1;
+        sl2[j] += e2;
+        sa[j] = fmaf(e1, d, sa[j]);
+      }
+    l1 = fmaf(a1, l1, (sl1[0] + sl1[1]) + (sl1[2] + sl1[3]));
+    l2 = fmaf(a2, l2, (sl2[0] + sl2[1]) + (sl2[2] + sl2[3]));
+    acc = fmaf(a1, acc, (sa[0] + sa[1]) + (sa[2] + sa[3]));
+  }
+
+  // merge the two lane halves: same query, disjoint key subsets
+  const float om1 = __shfl_xor(m1, 32), ol1 = __shfl_xor(l1, 32), oacc = __shfl_xor(acc, 32);
+  const float om2 = __shfl_xor(m2, 32), ol2 = __shfl_xor(l2, 32);
+  const float M1 = fmaxf(m1, om1), M2 = fmaxf(m2, om2);
+  const float w = fast_exp2((m1 - M1) * c), ow = fast_exp2((om1 - M1) * c);
+  const float v = fast_exp2((m2 - M2) * c), ov = fast_exp2((om2 - M2) * c);
+  const float L1 = l1 * w + ol1 * ow;
+  const float ACC = acc * w + oacc * ow;
+  const float L2 = l2 * v + ol2 * ov;
+  if (h == 0 && qrow < p.n_q) {
+    if (SPLIT) {
+      float* o = p.part + (((size_t)split * p.heads + head) * p.n_q + qrow) * 5;
+      o[0] = M1;
+      o[1] = L1;
+      o[2] = ACC;
+      o[3] = M2;
+      o[4] = L2;
+    } else {
+      const float lse1 = M1 * p.scale + log2f(L1) * kLn2;
+      const float lse2 = M2 * p.scale + log2f(L2) * kLn2;
+      p.kl[hq + qrow] = p.scale * ACC / L1 + lse2 - lse1;
+      p.lse1[hq + qrow] = lse1;
+      p.lse2[hq + qrow] = lse2;
+    }
+  }
+}
+
+// Merge the partial states of all key ranges of each row and finish the row.
+__global__ __launch_bounds__(256) void splitk_combine_kernel(FwdParams p) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int rows = p.heads * p.n_q;
+  if (i >= rows) return;
+  const float c = p.c;
+  float M1 = kMaxInit, M2 = kMaxInit;
+  for (int s = 0; s < p.splits; ++s) {
+    const float* st = p.part + ((size_t)s * rows + i) * 5;
+    M1 = fmaxf(M1, st[0]);
+    M2 = fmaxf(M2, st[3]);
+  }
+  float L1 = 0.f, L2 = 0.f, ACC = 0.f;
+  for (int s = 0; s < p.splits; ++s) {
+    const float* st = p.part + ((size_t)s * rows + i) * 5;
+    const float w1 = fast_exp2((st[0] - M1) * c);
+    const float w2 = fast_exp2((st[3] - M2) * c);
+    L1 = fmaf(st[1], w1, L1);
+    ACC = fmaf(st[2], w1, ACC);
+    L2 = fmaf(st[4], w2, L2);
+  }
+  const float lse1 = M1 * p.scale + log2f(L1) * kLn2;
+  const float lse2 = M2 * p.scale + log2f(L2) * kLn2;
+  p.kl[i] = p.scale * ACC / L1 + lse2 - lse1;
+  p.lse1[i] = lse1;
+  p.lse2[i] = lse2;
+}
+
+template <typename T, int D, int NW, bool SPLIT>
+static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
+  const int nqb = (p.n_q + 32 * NW - 1) / (32 * NW);
+  const long long blocks = (long long)p.heads * nqb * (SPLIT ? p.splits : 1);
+  hipLaunchKernelGGL((fwd_kernel<T, D, NW, SPLIT>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_nw(const FwdParams& p, int nw, bool split, hipStream_t stream) {
+  if (nw == 1) return split ? launch_one<T, D, 1, true>(p, stream) : launch_one<T, D, 1, false>(p, stream);
+  return split ? launch_one<T, D, 4, true>(p, stream) : launch_one<T, D, 4, false>(p, stream);
+}
+
+hipError_t launch_fwd(const FwdParams& p, int dtype, int head_dim, int nw, bool split, hipStream_t stream) {
+  if (dtype == 0) {
+    return head_dim == 64 ? launch_nw<__bf16, 64>(p, nw, split, stream)
+                          : launch_nw<__bf16, 128>(p, nw, split, stream);
+  }
+  return head_dim == 64 ? launch_nw<float, 64>(p, nw, split, stream)
+                        : launch_nw<float, 128>(p, nw, split, stream);
+}
+
+hipError_t launch_splitk_combine(const FwdParams& p, hipStream_t stream) {
+  const int rows = p.heads * p.n_q;
+  hipLaunchKernelGGL(splitk_combine_kernel, dim3((rows + 255) / 256), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace skl

@@ -1,0 +1,67 @@
+// Launch interface between the C ABI (api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+
+namespace skl {
+
+// Forward / split-K partial kernel arguments.
+struct FwdParams {
+  const char* q1;
+  const char* k1;
+  const char* q2;
+  const char* k2;
+  int n_q, n_k, heads, causal;
+  float scale;   // softmax scale
+  float c;       // scale * log2(e): exponent factor for exp2
+  float* kl;
+  float* lse1;
+  float* lse2;
+  float* part;      // split-K: partial states [splits][heads][n_q][5]
+  int splits;       // split-K: number of key ranges
+  int split_keys;   // split-K: keys per range (a multiple of the key tile)
+};
+
+// Key tile of the forward kernel (keys per LDS tile).
+constexpr int kFwdKeyTile = 64;
+
+// Queries per workgroup of the forward kernel for a given wave count.
+inline int fwd_queries_per_block(int nw) { return 32 * nw; }
+
+// Waves per workgroup the forward uses for n_q queries.
+inline int fwd_waves(int n_q) { return n_q <= 32 ? 1 : 4; }
+
+hipError_t launch_fwd(const FwdParams& p, int dtype, int head_dim, int nw, bool split,
+                      hipStream_t stream);
+hipError_t launch_splitk_combine(const FwdParams& p, hipStream_t stream);
+
+// Backward kernel arguments (both settings).
+struct BwdParams {
+  const char* q1;
+  const char* k1;
+  const char* q2;
+  const char* k2;
+  int n_q, n_k, heads, causal;
+  float scale, c;
+  const float* lse1;
+  const float* lse2;
+  const float* kl;    // Setting 2 only
+  const float* dkl;   // NULL = all ones
+  float* dq;          // gradient of the setting's Q (fp32)
+  float* dk;          // gradient of the setting's K (fp32)
+  int setting;        // 1 or 2
+  int dq_splits;      // separate path: key ranges of the dQ kernel (1 = plain stores)
+};
+
+hipError_t launch_bwd_separate(const BwdParams& p, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_bwd_fused(const BwdParams& p, int dtype, int head_dim, hipStream_t stream);
+
+// Whether the fused kernel's LDS footprint fits a workgroup for this dtype and head_dim.
+bool fused_supported(int dtype, int head_dim);
+
+// Queries per workgroup of the separate dQ kernel; keys per workgroup of the key-block kernels.
+constexpr int kBwdQueriesPerBlock = 128;
+constexpr int kBwdKeysPerBlock = 128;
+
+}  // namespace skl

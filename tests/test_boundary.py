@@ -1,0 +1,114 @@
+"""The C-ABI library on the CPU: it loads, exports every function that
+include/streamkl.h declares, and rejects invalid arguments with the documented
+status codes before anything is enqueued (no GPU is touched)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from streaming_kl_divergence_amd import _lib as L
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "streamkl.h")
+FAKE = 4096  # a non-NULL, 16-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(streamkl_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    lib = L.lib()
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.EXPORTS)
+
+
+def _fwd(**kw):
+    a = dict(q1=FAKE, k1=FAKE, q2=FAKE, k2=FAKE, n_q=16, n_k=16, heads=2, d=64, causal=0, scale=0.125, dt=L.BF16,
+             kl=FAKE, l1=FAKE, l2=FAKE)
+    a.update(kw)
+    return L.lib().streamkl_fwd(a["q1"], a["k1"], a["q2"], a["k2"], a["n_q"], a["n_k"], a["heads"], a["d"],
+                                a["causal"], a["scale"], a["dt"], a["kl"], a["l1"], a["l2"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q1=None), L.ERR_NULL), (dict(k2=None), L.ERR_NULL), (dict(kl=None), L.ERR_NULL),
+    (dict(n_q=0), L.ERR_SHAPE), (dict(n_k=-1), L.ERR_SHAPE), (dict(heads=0), L.ERR_SHAPE),
+    (dict(n_q=32, n_k=16, causal=1), L.ERR_SHAPE), (dict(heads=1 << 20, n_q=1 << 12), L.ERR_SHAPE),
+    (dict(d=96), L.ERR_UNSUPPORTED), (dict(d=256), L.ERR_UNSUPPORTED), (dict(dt=7), L.ERR_UNSUPPORTED),
+    (dict(scale=math.nan), L.ERR_SCALE), (dict(scale=math.inf), L.ERR_SCALE), (dict(scale=-1.0), L.ERR_SCALE),
+    (dict(q2=FAKE + 2), L.ERR_ALIGN),
+])
+def test_forward_validation(kw, code):
+    assert _fwd(**kw) == code
+
+
+def test_splitk_validation():
+    lib = L.lib()
+    args = [FAKE] * 4 + [1, 4096, 2, 128, 0, 0.1, L.BF16]
+    outs = [FAKE] * 3
+    need = lib.streamkl_workspace_bytes(0, 1, 4096, 2, 128, 4, 0)
+    assert need > 0 and need != ctypes.c_size_t(-1).value
+    assert lib.streamkl_fwd_splitk(*args, 4, *outs, None, need, None) == L.ERR_WORKSPACE
+    assert lib.streamkl_fwd_splitk(*args, 4, *outs, FAKE, need - 1, None) == L.ERR_WORKSPACE
+    assert lib.streamkl_fwd_splitk(*args, -1, *outs, FAKE, need, None) == L.ERR_UNSUPPORTED
+    assert lib.streamkl_fwd_splitk(*args, 2000, *outs, FAKE, need, None) == L.ERR_UNSUPPORTED
+    assert lib.streamkl_workspace_bytes(0, 1, 4096, 2, 96, 4, 0) == ctypes.c_size_t(-1).value
+    assert lib.streamkl_workspace_bytes(5, 1, 4096, 2, 128, 4, 0) == ctypes.c_size_t(-1).value
+    assert lib.streamkl_workspace_bytes(1, 1, 4096, 2, 128, 0, 9) == ctypes.c_size_t(-1).value
+    assert lib.streamkl_workspace_bytes(1, 1, 4096, 2, 128, 0, 0) == 0
+
+
+def test_splitk_auto_is_a_valid_split_count():
+    lib = L.lib()
+    for n_q, n_k in ((1, 524288), (1, 64), (37, 3000), (65536, 65536)):
+        s = lib.streamkl_splitk_auto(n_q, n_k, 32, 128)
+        assert 1 <= s <= 1024
+        # every range holds at least one key tile
+        assert (s - 1) * 64 < n_k
+
+
+def test_backward_validation():
+    lib = L.lib()
+    base = [FAKE] * 4 + [16, 16, 2, 64, 1, 0.125, L.BF16, FAKE, FAKE]
+    # Setting 1: lse1 lse2 dkl dq dk path ws wsb stream
+    assert lib.streamkl_bwd_set1(*base, None, FAKE, FAKE, 9, None, 0, None) == L.ERR_UNSUPPORTED
+    assert lib.streamkl_bwd_set1(*base, None, None, FAKE, 0, None, 0, None) == L.ERR_NULL
+    assert lib.streamkl_bwd_set1(*base, None, FAKE + 4, FAKE, 0, None, 0, None) == L.ERR_ALIGN
+    bad = list(base)
+    bad[11] = None  # lse1
+    assert lib.streamkl_bwd_set1(*bad, None, FAKE, FAKE, 0, None, 0, None) == L.ERR_NULL
+    # Setting 2 needs kl
+    assert lib.streamkl_bwd_set2(*base, None, None, FAKE, FAKE, 0, None, 0, None) == L.ERR_NULL
+    bad = list(base)
+    bad[4] = 32  # n_q > n_k with causal
+    assert lib.streamkl_bwd_set2(*bad, FAKE, None, FAKE, FAKE, 0, None, 0, None) == L.ERR_SHAPE
+
+
+def test_strerror_covers_every_code():
+    lib = L.lib()
+    for code in (L.OK, L.ERR_NULL, L.ERR_SHAPE, L.ERR_UNSUPPORTED, L.ERR_SCALE, L.ERR_WORKSPACE, L.ERR_HIP,
+                 L.ERR_ALIGN):
+        assert lib.streamkl_strerror(code) not in (None, b"unknown status")
+    assert lib.streamkl_strerror(12345) == b"unknown status"
+
+
+def test_bwd_select():
+    lib = L.lib()
+    # small dQ buffers (smallq128k: 32 x 512 x 128 fp32 = 8 MiB) use the fused kernel
+    assert lib.streamkl_bwd_select(512, 131072, 32, 128, 0) == L.BWD_FUSED
+    # large ones (causal64k: 1 GiB) use the separate kernels
+    assert lib.streamkl_bwd_select(65536, 65536, 32, 128, 1) == L.BWD_SEPARATE
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(L, "_lib", None)
+    monkeypatch.setattr(L, "LIB_PATH", "/nonexistent/libstreamkl.so")
+    with pytest.raises(ImportError):
+        L.lib()

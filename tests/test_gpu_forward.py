@@ -1,0 +1,125 @@
+"""GPU forward (fused one-pass and split-K) against the fp64 oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests.gpu_util import device_inputs, log, need_gpu, workload_device_inputs
+from tests.parity import compare
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_fwd(arrs, dtype, scale, causal, splits=None):
+    import torch
+    import streaming_kl_divergence_amd as skl
+    q1, k1, q2, k2 = device_inputs(arrs, dtype)
+    if splits is None:
+        out = skl.fwd(q1, k1, q2, k2, scale, causal)
+    else:
+        out = skl.fwd_splitk(q1, k1, q2, k2, scale, causal, num_splits=splits)
+    torch.cuda.synchronize()
+    return [o.cpu().numpy() for o in out]
+
+
+def _check_all_rows(arrs, dtype, scale, causal, splits=None, name=""):
+    kl, l1, l2 = _run_fwd(arrs, dtype, scale, causal, splits)
+    rkl, rl1, rl2 = oracle.forward(*arrs, scale, causal)
+    compare(l1, rl1, dtype, name + " lse1")
+    compare(l2, rl2, dtype, name + " lse2")
+    compare(kl, rkl, dtype, name + " kl", normwise=bool(np.abs(rkl).max() > 0))
+    return kl, rkl
+
+
+def test_tiny_fp32_config():
+    need_gpu()
+    w = W.WORKLOADS["tiny"]
+    log(f"case {w}")
+    _check_all_rows(W.all_inputs(w), "fp32", w.scale, w.causal, name="tiny")
+
+
+def _rand_case(seed, heads, n_q, n_k, d, dtype, corr=True):
+    rng = np.random.default_rng(seed)
+    q1 = rng.standard_normal((heads, n_q, d), dtype=np.float32)
+    k1 = rng.standard_normal((heads, n_k, d), dtype=np.float32)
+    q2 = rng.standard_normal((heads, n_q, d), dtype=np.float32)
+    k2 = rng.standard_normal((heads, n_k, d), dtype=np.float32)
+    if corr:
+        q2 = q1 + np.float32(0.3) * q2
+        k2 = k1 + np.float32(0.3) * k2
+    arrs = [q1, k1, q2, k2]
+    if dtype == "bf16":
+        arrs = [W.round_bf16(a) for a in arrs]
+    return arrs
+
+
+EDGE = [
+    # (heads, n_q, n_k, d, dtype, causal, scale_mult)
+    (2, 1000, 1000, 128, "bf16", True, 1.0),     # ragged tails, causal, several tiles
+    (2, 257, 1000, 128, "bf16", False, 1.0),     # ragged, non-causal, n_q != n_k
+    (2, 300, 1000, 128, "bf16", True, 1.0),      # causal bottom-right, n_q < n_k
+    (3, 200, 333, 64, "bf16", True, 1.0),        # d = 64
+    (2, 130, 190, 64, "fp32", True, 1.0),        # fp32 causal
+    (2, 100, 150, 128, "fp32", False, 1.0),      # fp32 d = 128
+    (4, 1, 777, 128, "bf16", False, 1.0),        # one query
+    (4, 1, 777, 128, "bf16", True, 1.0),         # one query, causal = full row
+    (2, 70, 1, 128, "bf16", False, 1.0),         # one key: KL = 0
+    (2, 500, 640, 128, "bf16", False, 0.0),      # scale 0: uniform rows, KL = 0
+    (2, 400, 900, 128, "bf16", True, 4.0),       # large logits (4 / sqrt(d))
+    (1, 64, 64, 128, "bf16", True, 1.0),         # exactly one tile
+]
+
+
+@pytest.mark.parametrize("idx", range(len(EDGE)), ids=[str(c) for c in EDGE])
+def test_edge_shapes(idx):
+    need_gpu()
+    case = EDGE[idx]
+    heads, n_q, n_k, d, dtype, causal, sm = case
+    log(f"case {case}")
+    arrs = _rand_case(100 + idx, heads, n_q, n_k, d, dtype, corr=(sm != 4.0))
+    _check_all_rows(arrs, dtype, sm / np.sqrt(d), causal, name=str(case))
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 0])
+def test_splitk_matches_oracle(splits):
+    need_gpu()
+    log(f"case splitk splits={splits}")
+    arrs = _rand_case(11, 3, 37, 3000, 128, "bf16", corr=False)
+    _check_all_rows(arrs, "bf16", 1 / np.sqrt(128), False, splits=splits, name=f"splits={splits}")
+    arrs = _rand_case(12, 2, 200, 1000, 128, "bf16")
+    _check_all_rows(arrs, "bf16", 1 / np.sqrt(128), True, splits=splits, name=f"causal splits={splits}")
+
+
+def test_splitk_equals_fused():
+    """Every split count gives the same rows as the one-pass kernel (to fp32 rounding)."""
+    need_gpu()
+    arrs = _rand_case(13, 2, 33, 5000, 128, "bf16", corr=False)
+    base = _run_fwd(arrs, "bf16", 0.09, False)
+    for s in (1, 3, 16, 0):
+        got = _run_fwd(arrs, "bf16", 0.09, False, splits=s)
+        for a, b in zip(got, base):
+            assert np.allclose(a, b, rtol=1e-4, atol=1e-5), s
+
+
+def test_causal8k_config():
+    """32 heads, 8K causal bf16 correlated: heads 0 and 31 in full, sampled rows of the rest."""
+    need_gpu()
+    import torch
+    import streaming_kl_divergence_amd as skl
+    w = W.WORKLOADS["causal8k"]
+    log(f"case {w}")
+    q1, k1, q2, k2 = workload_device_inputs(w)
+    kl, l1, l2 = [o.cpu().numpy() for o in skl.fwd(q1, k1, q2, k2, w.scale, w.causal)]
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    for h in range(w.heads):
+        a = W.head_inputs(w, h)
+        if h in (0, w.heads - 1):
+            rows = np.arange(w.n_q)
+        else:
+            rows = np.unique(np.concatenate([np.arange(70), w.n_q - 1 - np.arange(70),
+                                             rng.integers(0, w.n_q, 200), [127, 128, 129, 4095, 4096]]))
+        rkl, rl1, rl2 = oracle.forward_head(*a, w.scale, w.causal, rows)
+        compare(kl[h, rows], rkl, "bf16", f"h{h} kl")
+        compare(l1[h, rows], rl1, "bf16", f"h{h} lse1")
+        compare(l2[h, rows], rl2, "bf16", f"h{h} lse2")
