@@ -61,7 +61,11 @@ typedef enum { STREAMKL_BF16 = 0, STREAMKL_FP32 = 1 } streamkl_dtype;
 typedef enum {
   STREAMKL_BWD_AUTO = 0,      /* library chooses (see streamkl_bwd_select) */
   STREAMKL_BWD_FUSED = 1,     /* one kernel per (head, key block); dQ by fp32 atomics */
-  STREAMKL_BWD_SEPARATE = 2   /* a dK kernel and a dQ kernel, each recomputing P */
+  STREAMKL_BWD_SEPARATE = 2,  /* a dK kernel and a dQ kernel, each recomputing P */
+  STREAMKL_BWD_DK_ONLY = 3,   /* only the dK kernel of the separate path; dQ is not
+                                 written and may be NULL (e.g. queries frozen) */
+  STREAMKL_BWD_DQ_ONLY = 4    /* only the dQ kernel of the separate path; dK is not
+                                 written and may be NULL (e.g. keys frozen) */
 } streamkl_bwd_path;
 
 enum {
@@ -110,7 +114,8 @@ int streamkl_fwd_splitk(const void* q1, const void* k1, const void* q2, const vo
  * dk2 = scale dS2^T Q2 (fp32, [heads, n_q, head_dim] and [heads, n_k,
  * head_dim]), overwriting them.  lse1, lse2 are the forward's outputs for the
  * same inputs.  `path` picks the fused or separate kernels (AUTO: the
- * library's choice).  workspace: at least streamkl_workspace_bytes(1, ...)
+ * library's choice); DK_ONLY / DQ_ONLY compute one of the two gradients.
+ * Calling DK_ONLY then DQ_ONLY gives the same result as SEPARATE.  workspace: at least streamkl_workspace_bytes(1, ...)
  * bytes (may be NULL when that is 0).
  */
 int streamkl_bwd_set1(const void* q1, const void* k1, const void* q2, const void* k2,

@@ -11,7 +11,7 @@ LIB_PATH = os.path.join(PKG, "libstreamkl.so")
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_SCALE, ERR_WORKSPACE, ERR_HIP, ERR_ALIGN = -1, -2, -3, -4, -5, -6, -7
 BF16, FP32 = 0, 1
-BWD_AUTO, BWD_FUSED, BWD_SEPARATE = 0, 1, 2
+BWD_AUTO, BWD_FUSED, BWD_SEPARATE, BWD_DK_ONLY, BWD_DQ_ONLY = 0, 1, 2, 3, 4
 
 EXPORTS = ("streamkl_fwd", "streamkl_fwd_splitk", "streamkl_bwd_set1", "streamkl_bwd_set2",
            "streamkl_workspace_bytes", "streamkl_splitk_auto", "streamkl_bwd_select", "streamkl_strerror")

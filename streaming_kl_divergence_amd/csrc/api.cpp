@@ -109,8 +109,7 @@ size_t streamkl_workspace_bytes(int op, int n_q, int n_k, int heads, int head_di
     return (size_t)s * heads * n_q * 5 * sizeof(float);
   }
   if (op == 1 || op == 2) {
-    if (path != STREAMKL_BWD_AUTO && path != STREAMKL_BWD_FUSED && path != STREAMKL_BWD_SEPARATE)
-      return (size_t)-1;
+    if ((int)path < STREAMKL_BWD_AUTO || (int)path > STREAMKL_BWD_DQ_ONLY) return (size_t)-1;
     return 0;
   }
   return (size_t)-1;
@@ -180,10 +179,10 @@ static int bwd_common(int setting, const void* q1, const void* k1, const void* q
   (void)workspace_bytes;
   int st = check_common(q1, k1, q2, k2, n_q, n_k, heads, head_dim, causal, scale, (int)dtype);
   if (st) return st;
-  if (!lse1 || !lse2 || !dq || !dk || (setting == 2 && !kl)) return STREAMKL_ERR_NULL;
-  if (path != STREAMKL_BWD_AUTO && path != STREAMKL_BWD_FUSED && path != STREAMKL_BWD_SEPARATE)
-    return STREAMKL_ERR_UNSUPPORTED;
-  if (!aligned16(dq) || !aligned16(dk)) return STREAMKL_ERR_ALIGN;
+  if ((int)path < STREAMKL_BWD_AUTO || (int)path > STREAMKL_BWD_DQ_ONLY) return STREAMKL_ERR_UNSUPPORTED;
+  const bool want_dq = path != STREAMKL_BWD_DK_ONLY, want_dk = path != STREAMKL_BWD_DQ_ONLY;
+  if (!lse1 || !lse2 || (want_dq && !dq) || (want_dk && !dk) || (setting == 2 && !kl)) return STREAMKL_ERR_NULL;
+  if ((want_dq && !aligned16(dq)) || (want_dk && !aligned16(dk))) return STREAMKL_ERR_ALIGN;
   if (path == STREAMKL_BWD_AUTO) {
     path = (streamkl_bwd_path)streamkl_bwd_select(n_q, n_k, heads, head_dim, causal);
     if (path == STREAMKL_BWD_FUSED && !skl::fused_supported((int)dtype, head_dim)) path = STREAMKL_BWD_SEPARATE;
@@ -208,9 +207,9 @@ static int bwd_common(int setting, const void* q1, const void* k1, const void* q
   p.dq = dq;
   p.dk = dk;
   p.setting = setting;
-  p.dq_splits = path == STREAMKL_BWD_SEPARATE ? dq_splits_for(n_q, n_k, heads) : 1;
+  p.dq_splits = path == STREAMKL_BWD_FUSED ? 1 : dq_splits_for(n_q, n_k, heads);
   if (path == STREAMKL_BWD_FUSED) return status_of(skl::launch_bwd_fused(p, (int)dtype, head_dim, stream));
-  return status_of(skl::launch_bwd_separate(p, (int)dtype, head_dim, stream));
+  return status_of(skl::launch_bwd_separate(p, (int)dtype, head_dim, want_dk, want_dq, stream));
 }
 
 int streamkl_bwd_set1(const void* q1, const void* k1, const void* q2, const void* k2, int n_q, int n_k,

@@ -519,13 +519,17 @@ static hipError_t zero_fill(float* p, size_t n, hipStream_t s) {
 }
 
 template <typename T, int D, int SETTING>
-static hipError_t sep(const BwdParams& p, hipStream_t s) {
+static hipError_t sep(const BwdParams& p, bool do_dk, bool do_dq, hipStream_t s) {
   using KC = KvCfg<T, D>;
   using QC = QCfg<T, D>;
-  const int nkb = (p.n_k + KC::BKW - 1) / KC::BKW;
-  hipLaunchKernelGGL((bwd_kv_kernel<T, D, SETTING, false>), dim3(p.heads * nkb), dim3(256), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (do_dk) {
+    const int nkb = (p.n_k + KC::BKW - 1) / KC::BKW;
+    hipLaunchKernelGGL((bwd_kv_kernel<T, D, SETTING, false>), dim3(p.heads * nkb), dim3(256), 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (!do_dq) return e;
   const int nqb = (p.n_q + QC::BQ - 1) / QC::BQ;
   if (p.dq_splits > 1) {
     e = zero_fill(p.dq, (size_t)p.heads * p.n_q * D, s);
@@ -548,22 +552,24 @@ static hipError_t fused(const BwdParams& p, hipStream_t s) {
 }
 
 template <template <typename, int, int> class F>
-static hipError_t dispatch(const BwdParams& p, int dtype, int head_dim, hipStream_t s) {
+static hipError_t dispatch(const BwdParams& p, int dtype, int head_dim, int mode, hipStream_t s) {
   if (dtype == 0) {
-    if (head_dim == 64) return p.setting == 1 ? F<__bf16, 64, 1>::run(p, s) : F<__bf16, 64, 2>::run(p, s);
-    return p.setting == 1 ? F<__bf16, 128, 1>::run(p, s) : F<__bf16, 128, 2>::run(p, s);
+    if (head_dim == 64) return p.setting == 1 ? F<__bf16, 64, 1>::run(p, mode, s) : F<__bf16, 64, 2>::run(p, mode, s);
+    return p.setting == 1 ? F<__bf16, 128, 1>::run(p, mode, s) : F<__bf16, 128, 2>::run(p, mode, s);
   }
-  if (head_dim == 64) return p.setting == 1 ? F<float, 64, 1>::run(p, s) : F<float, 64, 2>::run(p, s);
-  return p.setting == 1 ? F<float, 128, 1>::run(p, s) : F<float, 128, 2>::run(p, s);
+  if (head_dim == 64) return p.setting == 1 ? F<float, 64, 1>::run(p, mode, s) : F<float, 64, 2>::run(p, mode, s);
+  return p.setting == 1 ? F<float, 128, 1>::run(p, mode, s) : F<float, 128, 2>::run(p, mode, s);
 }
 
 template <typename T, int D, int S>
 struct SepRun {
-  static hipError_t run(const BwdParams& p, hipStream_t s) { return sep<T, D, S>(p, s); }
+  static hipError_t run(const BwdParams& p, int mode, hipStream_t s) {
+    return sep<T, D, S>(p, (mode & 1) != 0, (mode & 2) != 0, s);
+  }
 };
 template <typename T, int D, int S>
 struct FusedRun {
-  static hipError_t run(const BwdParams& p, hipStream_t s) {
+  static hipError_t run(const BwdParams& p, int, hipStream_t s) {
     if constexpr (KvCfg<T, D>::kLdsFused > 160 * 1024) {
       return hipErrorNotSupported;
     } else {
@@ -572,12 +578,12 @@ struct FusedRun {
   }
 };
 
-hipError_t launch_bwd_separate(const BwdParams& p, int dtype, int head_dim, hipStream_t stream) {
-  return dispatch<SepRun>(p, dtype, head_dim, stream);
+hipError_t launch_bwd_separate(const BwdParams& p, int dtype, int head_dim, bool dk, bool dq, hipStream_t stream) {
+  return dispatch<SepRun>(p, dtype, head_dim, (dk ? 1 : 0) | (dq ? 2 : 0), stream);
 }
 
 hipError_t launch_bwd_fused(const BwdParams& p, int dtype, int head_dim, hipStream_t stream) {
-  return dispatch<FusedRun>(p, dtype, head_dim, stream);
+  return dispatch<FusedRun>(p, dtype, head_dim, 0, stream);
 }
 
 bool fused_supported(int dtype, int head_dim) {

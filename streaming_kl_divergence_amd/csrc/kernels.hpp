@@ -54,7 +54,7 @@ struct BwdParams {
   int dq_splits;      // separate path: key ranges of the dQ kernel (1 = plain stores)
 };
 
-hipError_t launch_bwd_separate(const BwdParams& p, int dtype, int head_dim, hipStream_t stream);
+hipError_t launch_bwd_separate(const BwdParams& p, int dtype, int head_dim, bool dk, bool dq, hipStream_t stream);
 hipError_t launch_bwd_fused(const BwdParams& p, int dtype, int head_dim, hipStream_t stream);
 
 // Whether the fused kernel's LDS footprint fits a workgroup for this dtype and head_dim.

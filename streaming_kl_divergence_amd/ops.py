@@ -8,7 +8,8 @@ import torch
 from . import _lib
 
 _DT = {torch.bfloat16: _lib.BF16, torch.float32: _lib.FP32}
-_PATH = {"auto": _lib.BWD_AUTO, "fused": _lib.BWD_FUSED, "separate": _lib.BWD_SEPARATE}
+_PATH = {"auto": _lib.BWD_AUTO, "fused": _lib.BWD_FUSED, "separate": _lib.BWD_SEPARATE,
+         "dk_only": _lib.BWD_DK_ONLY, "dq_only": _lib.BWD_DQ_ONLY}
 
 
 def _inputs(q1, k1, q2, k2):
@@ -75,11 +76,18 @@ def bwd_select(n_q, n_k, heads, head_dim, causal) -> str:
 
 
 def bwd(setting: int, q1, k1, q2, k2, scale: float, causal: bool, lse1, lse2, kl=None, dkl=None,
-        path: str = "auto"):
-    """(dQ, dK) of the setting's tensors (Setting 1: Q2, K2; Setting 2: Q1, K1), fp32."""
+        path: str = "auto", dq=None, dk=None):
+    """(dQ, dK) of the setting's tensors (Setting 1: Q2, K2; Setting 2: Q1, K1), fp32.
+
+    path: "auto", "fused", "separate", "dk_only" (dQ not computed, returned as
+    None) or "dq_only" (dK not computed).  dq / dk may be given as outputs."""
     heads, n_q, n_k, d, dt = _inputs(q1, k1, q2, k2)
-    dq = torch.empty(heads, n_q, d, device=q1.device, dtype=torch.float32)
-    dk = torch.empty(heads, n_k, d, device=q1.device, dtype=torch.float32)
+    if path not in _PATH:
+        raise ValueError(f"unknown path {path!r}")
+    if path != "dk_only" and dq is None:
+        dq = torch.empty(heads, n_q, d, device=q1.device, dtype=torch.float32)
+    if path != "dq_only" and dk is None:
+        dk = torch.empty(heads, n_k, d, device=q1.device, dtype=torch.float32)
     for t in (lse1, lse2, kl, dkl):
         if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or t.shape != (heads, n_q)):
             raise ValueError("lse1, lse2, kl, dkl must be contiguous fp32 [heads, n_q]")
@@ -87,11 +95,11 @@ def bwd(setting: int, q1, k1, q2, k2, scale: float, causal: bool, lse1, lse2, kl
     common = (q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), n_q, n_k, heads, d, int(causal),
               float(scale), dt, lse1.data_ptr(), lse2.data_ptr())
     if setting == 1:
-        st = L.streamkl_bwd_set1(*common, _ptr(dkl), dq.data_ptr(), dk.data_ptr(), _PATH[path], None, 0, _stream())
+        st = L.streamkl_bwd_set1(*common, _ptr(dkl), _ptr(dq), _ptr(dk), _PATH[path], None, 0, _stream())
     elif setting == 2:
         if kl is None:
             raise ValueError("Setting 2 needs the forward's KL rows")
-        st = L.streamkl_bwd_set2(*common, kl.data_ptr(), _ptr(dkl), dq.data_ptr(), dk.data_ptr(), _PATH[path],
+        st = L.streamkl_bwd_set2(*common, kl.data_ptr(), _ptr(dkl), _ptr(dq), _ptr(dk), _PATH[path],
                                  None, 0, _stream())
     else:
         raise ValueError("setting must be 1 or 2")

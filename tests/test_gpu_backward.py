@@ -89,6 +89,24 @@ def test_paths_agree():
             assert np.linalg.norm(x - y) <= 5e-3 * np.linalg.norm(x)
 
 
+def test_single_gradient_paths():
+    """DK_ONLY then DQ_ONLY equals SEPARATE, and each leaves the other gradient untouched."""
+    need_gpu()
+    import torch
+    import streaming_kl_divergence_amd as skl
+    arrs = _rand_case(22, 2, 300, 1100, 128, "bf16")
+    dev = device_inputs(arrs, "bf16")
+    kl, l1, l2 = skl.fwd(*dev, 0.09, True)
+    for setting in (1, 2):
+        ref_q, ref_k = skl.bwd(setting, *dev, 0.09, True, l1, l2, kl=kl, path="separate")
+        sentinel = torch.full_like(ref_q, 7.0)
+        dq, dk = skl.bwd(setting, *dev, 0.09, True, l1, l2, kl=kl, path="dk_only", dq=sentinel)
+        assert torch.equal(dq, torch.full_like(ref_q, 7.0)) and torch.equal(dk, ref_k)
+        sentinel = torch.full_like(ref_k, 7.0)
+        dq, dk = skl.bwd(setting, *dev, 0.09, True, l1, l2, kl=kl, path="dq_only", dk=sentinel)
+        assert torch.equal(dk, torch.full_like(ref_k, 7.0)) and torch.equal(dq, ref_q)
+
+
 def test_causal8k_setting1_config():
     """32 heads, 8K causal bf16 correlated, Setting 1: heads 0 and 31 in full
     against the oracle; every head checked for sum_j dK_j = 0 and
