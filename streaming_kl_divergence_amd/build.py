@@ -36,9 +36,14 @@ def flags() -> list[str]:
             "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
+# MFMA results stay in VGPRs: the VALU reads every score, and a result in an
+# AGPR would cost one v_accvgpr_read per value
+EXTRA = {"fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
-    cmd = [hipcc(), *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *flags(), *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the device-only feature flag; that note is harmless
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)

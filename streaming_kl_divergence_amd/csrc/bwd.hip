@@ -120,6 +120,27 @@ __device__ __forceinline__ f32x16 kgroup_mfma<float>(const SKL_LDS char* xrow, i
   return acc;
 }
 
+// bf16 form of kgroup_mfma: the A operand (X^T rows = 32 columns of the
+// row-major LDS tile starting at element column c0; k = tile rows rbase ..
+// rbase+31) comes straight from the row-major tile through transposing reads.
+template <int D>
+__device__ __forceinline__ f32x16 kgroup_mfma_tr(const SKL_LDS char* tile, int rbase, int c0, int lane,
+                                                 const float* v, f32x16 acc) {
+  const int h = lane >> 5;
+  const int cl = c0 + 16 * ((lane >> 4) & 1);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const u32x2 lo = read_tr4<D>(tile, rbase + 16 * t + 4 * h, cl, lane);
+    const u32x2 hi = read_tr4<D>(tile, rbase + 16 * t + 8 + 4 * h, cl, lane);
+    const u32x4 a = u32x4{lo.x, lo.y, hi.x, hi.y};
+    bf16x8 b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) b[e] = (__bf16)v[8 * t + e];
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), b, acc, 0, 0, 0);
+  }
+  return acc;
+}
+
 // ---- per-row coefficients --------------------------------------------------------
 // Setting 1: (LSE1 log2e, LSE2 log2e, g)            dS = g (2^(x2 c - b) - 2^(x1 c - a))
 // Setting 2: (LSE1 log2e, g scale, -g (LSE1 - LSE2 + KL))
@@ -156,10 +177,12 @@ struct KvCfg {
   static constexpr int BT = (sizeof(T) == 4 && D == 128) ? 32 : 64;      // queries per tile
   static constexpr int NQB = BT / 32;
   static constexpr int TILE = BT * Geom<T, D>::kRowBytes;
+  static constexpr bool TR = sizeof(T) == 2;   // bf16: transposing reads; fp32: a transposed copy
   using QT = TGeom<T, D, BT, 8>;
   using KT = TGeom<T, D, BKW, 16>;
   using DS = TGeom<T, BT, BKW, 16>;   // dS rows: [query][key]
-  static constexpr int kLdsBase = 4 * TILE + QT::kBytes + 3 * BT * 4;
+  static constexpr int kQtBytes = TR ? 0 : QT::kBytes;
+  static constexpr int kLdsBase = 4 * TILE + kQtBytes + 2 * 3 * BT * 4;
   static constexpr int kLdsFused = kLdsBase + KT::kBytes + DS::kBytes;
 };
 
@@ -170,9 +193,9 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
   constexpr int NW = C::NW, BT = C::BT, NQB = C::NQB, TILE = C::TILE, DB = D / 32;
   __shared__ __attribute__((aligned(16))) char smem[FUSED ? C::kLdsFused : C::kLdsBase];
   SKL_LDS char* lds = (SKL_LDS char*)smem;
-  SKL_LDS char* qt = lds + 4 * TILE;
-  SKL_LDS float* coef = (SKL_LDS float*)(qt + C::QT::kBytes);
-  SKL_LDS char* kt = (SKL_LDS char*)(coef + 3 * BT);
+  SKL_LDS char* qt = lds + 4 * TILE;                                    // fp32 only
+  SKL_LDS float* coef = (SKL_LDS float*)(qt + C::kQtBytes);             // [2][3][BT]
+  SKL_LDS char* kt = (SKL_LDS char*)(coef + 2 * 3 * BT);
   SKL_LDS char* dst = kt + C::KT::kBytes;
 
   const int tid = threadIdx.x;
@@ -193,7 +216,6 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
   const size_t hk = (size_t)head * p.n_k;
   const char* q1 = p.q1 + hq * G::kRowBytes;
   const char* q2 = p.q2 + hq * G::kRowBytes;
-  const char* qs = SETTING == 1 ? q2 : q1;   // the setting's Q (for dK)
   const char* ks = (SETTING == 1 ? p.k2 : p.k1) + hk * G::kRowBytes;
 
   // this lane's key row: chunks 2g + h of K1 and K2
@@ -226,95 +248,98 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
   const int ntiles = (p.n_q + BT - 1) / BT - t0;
   const bool wave_idle = kw0 >= p.n_k;
 
+  auto load_coefs = [&](int q0, SKL_LDS float* cf) {
+    if (tid < BT) {
+      float a = 0.f, b = 0.f, c3 = 0.f;
+      if (q0 + tid < p.n_q) row_coefs<SETTING>(p, hq + q0 + tid, a, b, c3);
+      cf[tid] = a;
+      cf[BT + tid] = b;
+      cf[2 * BT + tid] = c3;
+    }
+  };
   if (ntiles > 0) {
     issue_tile_async<T, D, BT, NW>(q1, t0 * BT, p.n_q, lds, tid, wave);
     issue_tile_async<T, D, BT, NW>(q2, t0 * BT, p.n_q, lds + TILE, tid, wave);
+    load_coefs(t0 * BT, coef);
   }
   for (int t = 0; t < ntiles; ++t) {
     const int q0 = (t0 + t) * BT;
     const int buf = t & 1;
     const SKL_LDS char* t1 = lds + buf * 2 * TILE;
     const SKL_LDS char* t2 = t1 + TILE;
+    const SKL_LDS float* cf = coef + buf * 3 * BT;
     wait_async_loads();
-    __syncthreads();  // tile t visible; previous tile's LDS readers done
+    __syncthreads();  // tile t and its coefficients visible; tile t-1's readers done
     if (t + 1 < ntiles) {
       SKL_LDS char* nb = lds + (buf ^ 1) * 2 * TILE;
       issue_tile_async<T, D, BT, NW>(q1, q0 + BT, p.n_q, nb, tid, wave);
       issue_tile_async<T, D, BT, NW>(q2, q0 + BT, p.n_q, nb + TILE, tid, wave);
+      load_coefs(q0 + BT, coef + (buf ^ 1) * 3 * BT);
     }
-    const SKL_LDS char* tsrc = SETTING == 1 ? t2 : t1;
-    build_transposed<T, D, BT, 8, NW * 64>(qt, tid, [&](int r, int cc) {
-      return *(const SKL_LDS u32x4*)(tsrc + lds_chunk_off<T, D>(r, cc));
-    });
-    if (tid < BT) {
-      float a = 0.f, b = 0.f, c3 = 0.f;
-      if (q0 + tid < p.n_q) row_coefs<SETTING>(p, hq + q0 + tid, a, b, c3);
-      coef[tid] = a;
-      coef[BT + tid] = b;
-      coef[2 * BT + tid] = c3;
+    const SKL_LDS char* tsrc = SETTING == 1 ? t2 : t1;   // the setting's Q
+    if constexpr (!C::TR) {
+      build_transposed<T, D, BT, 8, NW * 64>(qt, tid, [&](int r, int cc) {
+        return *(const SKL_LDS u32x4*)(tsrc + lds_chunk_off<T, D>(r, cc));
+      });
+      __syncthreads();
     }
-    __syncthreads();
 
     const int qlast = min(q0 + BT, p.n_q) - 1;
     const bool skip = wave_idle || (p.causal && kw0 > qlast + off);
-    float ds[NQB][16];
-    if (!skip) {
-      f32x16 s1[NQB], s2[NQB];
+    const bool need_mask = (q0 + BT > p.n_q) || (kw0 + 32 > p.n_k) || (p.causal && kw0 + 31 > q0 + off);
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        s1[qb] = f32x16{};
-        s2[qb] = f32x16{};
+    for (int qb = 0; qb < NQB; ++qb) {
+      float ds[16];
+      if (!skip) {
+        f32x16 s1 = f32x16{}, s2 = f32x16{};
 #pragma unroll
         for (int g = 0; g < G::kGroups; ++g) {
           const int ob = lds_chunk_off<T, D>(qb * 32 + col, 2 * g + h);
-          s1[qb] = mfma_chunk<T>(*(const SKL_LDS u32x4*)(t1 + ob), kf1[g], s1[qb]);
-          s2[qb] = mfma_chunk<T>(*(const SKL_LDS u32x4*)(t2 + ob), kf2[g], s2[qb]);
+          s1 = mfma_chunk<T>(*(const SKL_LDS u32x4*)(t1 + ob), kf1[g], s1);
+          s2 = mfma_chunk<T>(*(const SKL_LDS u32x4*)(t2 + ob), kf2[g], s2);
         }
-      }
-      const bool need_mask = (q0 + BT > p.n_q) || (kw0 + 32 > p.n_k) || (p.causal && kw0 + 31 > q0 + off);
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const int qi = qb * 32 + 8 * m + 4 * h;   // first of four consecutive queries
-          const f32x4 ca = *(const SKL_LDS f32x4*)(coef + qi);
-          const f32x4 cb = *(const SKL_LDS f32x4*)(coef + BT + qi);
-          const f32x4 cc = *(const SKL_LDS f32x4*)(coef + 2 * BT + qi);
+          const f32x4 ca = *(const SKL_LDS f32x4*)(cf + qi);
+          const f32x4 cb = *(const SKL_LDS f32x4*)(cf + BT + qi);
+          const f32x4 cc = *(const SKL_LDS f32x4*)(cf + 2 * BT + qi);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * m + e;
-            float v = dlogit<SETTING>(s1[qb][r], s2[qb][r], c, ca[e], cb[e], cc[e]);
+            float v = dlogit<SETTING>(s1[r], s2[r], c, ca[e], cb[e], cc[e]);
             if (need_mask) {
               const int q = q0 + qi + e;
               const bool ok = q < p.n_q && key < p.n_k && (!p.causal || key <= q + off);
               v = ok ? v : 0.f;
             }
-            ds[qb][r] = v;
+            ds[r] = v;
           }
         }
-      // dK^T(d, keys) += Q^T(d, queries) dS(queries, keys)
+        // dK^T(d, keys) += Q^T(d, queries) dS(queries, keys)
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
+        for (int db = 0; db < DB; ++db) {
+          if constexpr (C::TR)
+            dkt[db] = kgroup_mfma_tr<D>(tsrc, qb * 32, db * 32, lane, ds, dkt[db]);
+          else
+            dkt[db] = kgroup_mfma<T>(qt + (db * 32 + col) * C::QT::kStride, qb * 32, h, ds, dkt[db]);
+        }
+      } else {
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-          dkt[db] = kgroup_mfma<T>(qt + (db * 32 + col) * C::QT::kStride, qb * 32, h, ds[qb], dkt[db]);
-    } else {
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) ds[qb][r] = 0.f;
-    }
-
-    if (FUSED) {
-      // dS block -> LDS as [query][key]
-      const int kl = wave * 32 + col;
-#pragma unroll
-      for (int qb = 0; qb < NQB; ++qb)
+        for (int r = 0; r < 16; ++r) ds[r] = 0.f;
+      }
+      if (FUSED) {
+        // this dS block -> LDS as [query][key]
+        const int kl = wave * 32 + col;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int ql = qb * 32 + acc_row(r, h);
-          *(SKL_LDS T*)(dst + ql * C::DS::kStride + kl * (int)sizeof(T)) = (T)ds[qb][r];
+          *(SKL_LDS T*)(dst + ql * C::DS::kStride + kl * (int)sizeof(T)) = (T)ds[r];
         }
+      }
+    }
+
+    if (FUSED) {
       __syncthreads();
       // dQ(queries, d) = dS(queries, keys) K(keys, d) over this block's keys
       constexpr int NB = NQB * DB;
@@ -359,8 +384,9 @@ struct QCfg {
   static constexpr int BK = (sizeof(T) == 4 && D == 128) ? 32 : 64;
   static constexpr int NKB = BK / 32;
   static constexpr int TILE = BK * Geom<T, D>::kRowBytes;
+  static constexpr bool TR = sizeof(T) == 2;
   using KT = TGeom<T, D, BK, 8>;
-  static constexpr int kLds = 4 * TILE + KT::kBytes;
+  static constexpr int kLds = 4 * TILE + (TR ? 0 : KT::kBytes);
 };
 
 template <typename T, int D, int SETTING, bool SPLIT>
@@ -370,7 +396,7 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdParams p) {
   constexpr int NW = C::NW, BQ = C::BQ, BK = C::BK, NKB = C::NKB, TILE = C::TILE, DB = D / 32;
   __shared__ __attribute__((aligned(16))) char smem[C::kLds];
   SKL_LDS char* lds = (SKL_LDS char*)smem;
-  SKL_LDS char* kt = lds + 4 * TILE;
+  SKL_LDS char* kt = lds + 4 * TILE;   // fp32 only
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -403,6 +429,12 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdParams p) {
   int kend = klimit;
   if (p.causal) kend = min(kend, min(q0 + BQ, p.n_q) + off);
   const int ntiles = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+  int wtiles = 0;
+  if (qw0 < p.n_q) {
+    const int wend = p.causal ? min(klimit, min(qw0 + 32, p.n_q) + off) : klimit;
+    wtiles = wend > kbeg ? min(ntiles, (wend - kbeg + BK - 1) / BK) : 0;
+  }
+  wtiles = __builtin_amdgcn_readfirstlane(wtiles);
 
   const size_t hq = (size_t)head * p.n_q;
   const size_t hk = (size_t)head * p.n_k;
@@ -426,8 +458,6 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdParams p) {
   f32x16 dqt[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) dqt[i] = f32x16{};
-  const int wlast = min(qw0 + 31, p.n_q - 1);
-  const bool wave_idle = qw0 >= p.n_q;
 
   if (ntiles > 0) {
     issue_tile_async<T, D, BK, NW>(k1, kbeg, p.n_k, lds, tid, wave);
@@ -444,46 +474,45 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdParams p) {
       issue_tile_async<T, D, BK, NW>(k1, kbeg + (t + 1) * BK, p.n_k, nb, tid, wave);
       issue_tile_async<T, D, BK, NW>(k2, kbeg + (t + 1) * BK, p.n_k, nb + TILE, tid, wave);
     }
-    const SKL_LDS char* tsrc = SETTING == 1 ? t2 : t1;
-    build_transposed<T, D, BK, 8, NW * 64>(kt, tid, [&](int r, int cc2) {
-      return *(const SKL_LDS u32x4*)(tsrc + lds_chunk_off<T, D>(r, cc2));
-    });
-    __syncthreads();
-
+    const SKL_LDS char* tsrc = SETTING == 1 ? t2 : t1;   // the setting's K
+    if constexpr (!C::TR) {
+      build_transposed<T, D, BK, 8, NW * 64>(kt, tid, [&](int r, int cc2) {
+        return *(const SKL_LDS u32x4*)(tsrc + lds_chunk_off<T, D>(r, cc2));
+      });
+      __syncthreads();
+    }
+    if (t >= wtiles) continue;  // wave-uniform: past this wave's frontier
     const int k0 = kbeg + t * BK;
-    if (wave_idle || (p.causal && k0 > wlast + off)) continue;
-    f32x16 s1[NKB], s2[NKB];
+    const bool need_mask = (k0 + BK > klimit) || (qw0 + 32 > p.n_q) || (p.causal && k0 + BK - 1 > qw0 + off);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      s1[kb] = f32x16{};
-      s2[kb] = f32x16{};
+      f32x16 s1 = f32x16{}, s2 = f32x16{};
 #pragma unroll
       for (int g = 0; g < G::kGroups; ++g) {
         const int ob = lds_chunk_off<T, D>(kb * 32 + col, 2 * g + h);
-        s1[kb] = mfma_chunk<T>(*(const SKL_LDS u32x4*)(t1 + ob), qf1[g], s1[kb]);
-        s2[kb] = mfma_chunk<T>(*(const SKL_LDS u32x4*)(t2 + ob), qf2[g], s2[kb]);
+        s1 = mfma_chunk<T>(*(const SKL_LDS u32x4*)(t1 + ob), qf1[g], s1);
+        s2 = mfma_chunk<T>(*(const SKL_LDS u32x4*)(t2 + ob), qf2[g], s2);
       }
-    }
-    const bool need_mask = (k0 + BK > klimit) || (qw0 + 32 > p.n_q) || (p.causal && k0 + BK - 1 > qw0 + off);
-    float ds[NKB][16];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float v = dlogit<SETTING>(s1[kb][r], s2[kb][r], c, ca, cb, cc);
+        float v = dlogit<SETTING>(s1[r], s2[r], c, ca, cb, cc);
         if (need_mask) {
           const int kk = k0 + kb * 32 + acc_row(r, h);
           const bool ok = kk < klimit && qrow < p.n_q && (!p.causal || kk <= qrow + off);
           v = ok ? v : 0.f;
         }
-        ds[kb][r] = v;
+        ds[r] = v;
       }
-    // dQ^T(d, queries) += K^T(d, keys) dS^T(keys, queries)
+      // dQ^T(d, queries) += K^T(d, keys) dS^T(keys, queries)
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-        dqt[db] = kgroup_mfma<T>(kt + (db * 32 + col) * C::KT::kStride, kb * 32, h, ds[kb], dqt[db]);
+      for (int db = 0; db < DB; ++db) {
+        if constexpr (C::TR)
+          dqt[db] = kgroup_mfma_tr<D>(tsrc, kb * 32, db * 32, lane, ds, dqt[db]);
+        else
+          dqt[db] = kgroup_mfma<T>(kt + (db * 32 + col) * C::KT::kStride, kb * 32, h, ds, dqt[db]);
+      }
+    }
   }
 
   if (qrow < p.n_q) {

@@ -1,9 +1,14 @@
 // Shared device helpers for the attention-KL kernels on gfx950 (CDNA4).
 //
 // Tiles of K (or Q) rows live in LDS as rows of 16-byte chunks.  A chunk's
-// slot inside its row is XOR-swizzled with the low bits of the row index, so
-// that the 32-row MFMA operand reads (one 16-byte chunk per lane, 16 lanes per
-// LDS cycle) hit 16 distinct chunk slots and never conflict on a bank.
+// slot inside its row is XOR-swizzled with a function of the row index that
+// serves both read patterns of the kernels:
+//   * MFMA operand reads (one 16-byte chunk per lane, rows r .. r+15 at the
+//     same logical chunk): the 16 rows get 16 distinct slots;
+//   * transposing reads (ds_read_b64_tr_b16: four consecutive rows, one
+//     aligned pair of chunks): the XOR keeps each pair together and moves the
+//     four rows to four distinct pairs.
+// So neither pattern conflicts on a bank.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -31,15 +36,22 @@ struct Geom {
   static constexpr int kRowBytes = D * (int)sizeof(T);
   static constexpr int kChunks = kRowBytes / 16;          // 16-byte chunks per row
   static constexpr int kGroups = kChunks / 2;             // chunk pairs (one per lane half)
-  static constexpr int kSwz = (kChunks < 16 ? kChunks : 16) - 1;
   static_assert(kChunks >= 8, "rows must be at least 128 bytes");
 };
+
+// Swizzle of row `row`: ((row mod 8) << 1 | bit 3 of row) for rows of 16 or
+// more chunks, ((row mod 4) << 1 | bit 2 of row) for rows of 8 chunks.
+template <int kChunks>
+__device__ __forceinline__ int row_swizzle(int row) {
+  if constexpr (kChunks >= 16) return ((row & 7) << 1) | ((row >> 3) & 1);
+  else return ((row & 3) << 1) | ((row >> 2) & 1);
+}
 
 // Byte offset of chunk `c` of tile row `row` inside an LDS tile.
 template <typename T, int D>
 __device__ __forceinline__ int lds_chunk_off(int row, int c) {
   using G = Geom<T, D>;
-  return (row * G::kChunks + (c ^ (row & G::kSwz))) * 16;
+  return (row * G::kChunks + (c ^ row_swizzle<G::kChunks>(row))) * 16;
 }
 
 // acc(32 x 32) += A(32 x k) B(k x 32) for one chunk pair.  Lane l supplies one
@@ -92,7 +104,7 @@ __device__ __forceinline__ void issue_tile_async(const char* __restrict__ g, int
     const int slot = i * NW * 64 + tid;
     const int row = slot / G::kChunks;
     const int pc = slot % G::kChunks;
-    const int c = pc ^ (row & G::kSwz);
+    const int c = pc ^ row_swizzle<G::kChunks>(row);
     const int src_row = min(key0 + row, n_rows - 1);
     const char* src = g + (size_t)src_row * G::kRowBytes + c * 16;
     // lane i of this wave lands at base + 16 * i
@@ -102,5 +114,22 @@ __device__ __forceinline__ void issue_tile_async(const char* __restrict__ g, int
 }
 
 __device__ __forceinline__ void wait_async_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Transposing LDS read (bf16 tiles): lane l of each 16-lane group passes the
+// address of element (r0 + (l % 16) / 4, c0 + 4 * (l % 4)) of a row-major
+// tile and receives the four elements (r0 + e, c0 + l % 16), e = 0..3: four
+// consecutive rows of one column.  (Measured lane semantics of
+// ds_read_b64_tr_b16 on gfx950: result[i][e] = loaded[4e + i/4][i % 4]
+// within each group of 16 lanes.)
+template <int D>
+__device__ __forceinline__ u32x2 read_tr4(const SKL_LDS char* tile, int r0, int c0, int lane) {
+  const int l16 = lane & 15;
+  const int row = r0 + (l16 >> 2);
+  const int cc = c0 + 4 * (l16 & 3);            // bf16 element column
+  const int off = lds_chunk_off<__bf16, D>(row, cc >> 3) + (cc & 7) * 2;
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SKL_LDS s16x4*)(tile + off));
+  return __builtin_bit_cast(u32x2, v);
+}
 
 }  // namespace skl

@@ -35,6 +35,83 @@
 
 namespace skl {
 
+// Running five-scalar state of one lane (one query, half of the keys).
+struct RowState {
+  float m1, m2, l1, l2, acc;
+};
+
+// S1, S2 (raw units) of one 64-key tile for this lane's query: 2 blocks of 16.
+template <typename T, int D, int NKB>
+__device__ __forceinline__ void tile_scores(const SKL_LDS char* t1, const SKL_LDS char* t2, const u32x4* qf1,
+                                            const u32x4* qf2, int col, int h, f32x16* s1, f32x16* s2) {
+  using G = Geom<T, D>;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) {
+    s1[kb] = f32x16{};
+    s2[kb] = f32x16{};
+#pragma unroll
+    for (int g = 0; g < G::kGroups; ++g) {
+      const int ob = lds_chunk_off<T, D>(kb * 32 + col, 2 * g + h);
+      s1[kb] = mfma_chunk<T>(*(const SKL_LDS u32x4*)(t1 + ob), qf1[g], s1[kb]);
+      s2[kb] = mfma_chunk<T>(*(const SKL_LDS u32x4*)(t2 + ob), qf2[g], s2[kb]);
+    }
+  }
+}
+
+// Fold one tile of scores into the running state.  MASK: the tile crosses the
+// causal diagonal or the end of the key range, so some pairs are excluded.
+template <bool MASK, int NKB>
+__device__ __forceinline__ void tile_update(RowState& st, f32x16* s1, f32x16* s2, float c, int k0, int h,
+                                            int klimit, int causal, int qlim) {
+  if (MASK) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + kb * 32 + acc_row(r, h);
+        const bool ok = key < klimit && (!causal || key <= qlim);
+        s1[kb][r] = ok ? s1[kb][r] : -INFINITY;
+        s2[kb][r] = ok ? s2[kb][r] : -INFINITY;
+      }
+  }
+  float tm1 = -INFINITY, tm2 = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      tm1 = fmaxf(tm1, s1[kb][r]);
+      tm2 = fmaxf(tm2, s2[kb][r]);
+    }
+  const float n1 = fmaxf(st.m1, tm1), n2 = fmaxf(st.m2, tm2);
+  const float a1 = fast_exp2((st.m1 - n1) * c), a2 = fast_exp2((st.m2 - n2) * c);
+  st.m1 = n1;
+  st.m2 = n2;
+  const float mc1 = n1 * c, mc2 = n2 * c;
+  float sl1[4] = {0.f, 0.f, 0.f, 0.f}, sl2[4] = {0.f, 0.f, 0.f, 0.f}, sa[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float x1 = s1[kb][r], x2 = s2[kb][r];
+      float e1 = fast_exp2(fmaf(x1, c, -mc1));
+      float e2 = fast_exp2(fmaf(x2, c, -mc2));
+      float d = x1 - x2;
+      if (MASK) {
+        const bool ok = x1 != -INFINITY;  // real scores are finite
+        e1 = ok ? e1 : 0.f;
+        e2 = ok ? e2 : 0.f;
+        d = ok ? d : 0.f;
+      }
+      const int j = r & 3;
+      sl1[j] += e1;
+      sl2[j] += e2;
+      sa[j] = fmaf(e1, d, sa[j]);
+    }
+  st.l1 = fmaf(a1, st.l1, (sl1[0] + sl1[1]) + (sl1[2] + sl1[3]));
+  st.l2 = fmaf(a2, st.l2, (sl2[0] + sl2[1]) + (sl2[2] + sl2[3]));
+  st.acc = fmaf(a1, st.acc, (sa[0] + sa[1]) + (sa[2] + sa[3]));
+}
+
 template <typename T, int D, int NW, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   using G = Geom<T, D>;
@@ -76,6 +153,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   int kend = klimit;
   if (p.causal) kend = min(kend, min(q0 + BQ, p.n_q) + off);
   const int ntiles = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+  // tiles holding at least one key visible to this wave's real queries
+  int wtiles = 0;
+  if (qw0 < p.n_q) {
+    const int wend = p.causal ? min(klimit, min(qw0 + 32, p.n_q) + off) : klimit;
+    wtiles = wend > kbeg ? min(ntiles, (wend - kbeg + BK - 1) / BK) : 0;
+  }
+  wtiles = __builtin_amdgcn_readfirstlane(wtiles);
 
   const size_t hq = (size_t)head * p.n_q;
   const size_t hk = (size_t)head * p.n_k;
@@ -95,106 +179,45 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
     }
   }
 
-  float m1 = kMaxInit, m2 = kMaxInit, l1 = 0.f, l2 = 0.f, acc = 0.f;
+  RowState st{kMaxInit, kMaxInit, 0.f, 0.f, 0.f};
   const float c = p.c;
-  // the wave's last real query; waves past n_q have nothing to compute
-  const int wlast = min(qw0 + 31, p.n_q - 1);
-  const bool wave_idle = qw0 >= p.n_q;
+  const int qlim = qrow + off;   // last key this lane's query may see (causal)
 
+  // Two waves per SIMD (223 VGPRs) overlap one wave's MFMAs with the other's VALU.
+  f32x16 s1[NKB], s2[NKB];
   if (ntiles > 0) {
     issue_tile_async<T, D, BK, NW>(k1, kbeg, p.n_k, lds, tid, wave);
     issue_tile_async<T, D, BK, NW>(k2, kbeg, p.n_k, lds + TILE, tid, wave);
   }
   for (int t = 0; t < ntiles; ++t) {
     wait_async_loads();
-    __syncthreads();  // tile t visible to all waves; buffer t+1 free again
+    __syncthreads();  // tile t visible; buffer t+1 free again
     const int buf = t & 1;
     if (t + 1 < ntiles) {
       SKL_LDS char* nb = lds + (buf ^ 1) * 2 * TILE;
       issue_tile_async<T, D, BK, NW>(k1, kbeg + (t + 1) * BK, p.n_k, nb, tid, wave);
       issue_tile_async<T, D, BK, NW>(k2, kbeg + (t + 1) * BK, p.n_k, nb + TILE, tid, wave);
     }
+    if (t >= wtiles) continue;
     const int k0 = kbeg + t * BK;
-    if (wave_idle || (p.causal && k0 > wlast + off)) continue;  // wave-uniform
-
-    const SKL_LDS char* t1 = lds + buf * 2 * TILE;
-    const SKL_LDS char* t2 = t1 + TILE;
-    f32x16 s1[NKB], s2[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      s1[kb] = f32x16{};
-      s2[kb] = f32x16{};
-#pragma unroll
-      for (int g = 0; g < G::kGroups; ++g) {
-        const int off_b = lds_chunk_off<T, D>(kb * 32 + col, 2 * g + h);
-        const u32x4 a1 = *(const SKL_LDS u32x4*)(t1 + off_b);
-        const u32x4 a2 = *(const SKL_LDS u32x4*)(t2 + off_b);
-        s1[kb] = mfma_chunk<T>(a1, qf1[g], s1[kb]);
-        s2[kb] = mfma_chunk<T>(a2, qf2[g], s2[kb]);
-      }
-    }
-
     const bool need_mask = (k0 + BK > klimit) || (p.causal && k0 + BK - 1 > qw0 + off);
-    if (need_mask) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + kb * 32 + acc_row(r, h);
-          const bool ok = key < klimit && (!p.causal || key <= qrow + off);
-          if (!ok) {
-            s1[kb][r] = -INFINITY;
-            s2[kb][r] = -INFINITY;
-          }
-        }
-    }
-    float tm1 = -INFINITY, tm2 = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        tm1 = fmaxf(tm1, s1[kb][r]);
-        tm2 = fmaxf(tm2, s2[kb][r]);
-      }
-    const float n1 = fmaxf(m1, tm1), n2 = fmaxf(m2, tm2);
-    const float a1 = fast_exp2((m1 - n1) * c), a2 = fast_exp2((m2 - n2) * c);
-    m1 = n1;
-    m2 = n2;
-    const float mc1 = n1 * c, mc2 = n2 * c;
-    float sl1[4] = {0.f, 0.f, 0.f, 0.f}, sl2[4] = {0.f, 0.f, 0.f, 0.f}, sa[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float x1 = s1[kb][r], x2 = s2[kb][r];
-        float e1 = fast_exp2(fmaf(x1, c, -mc1));
-        float e2 = fast_exp2(fmaf(x2, c, -mc2));
-        float d = x1 - x2;
-        if (need_mask) {
-          const bool ok = x1 != -INFINITY;  // real scores are finite
-          e1 = ok ? e1 : 0.f;
-          e2 = ok ? e2 : 0.f;
-          d = ok ? d : 0.f;
-        }
-        const int j = r & 3;
-        sl1[j] += e1;
-        sl2[j] += e2;
-        sa[j] = fmaf(e1, d, sa[j]);
-      }
-    l1 = fmaf(a1, l1, (sl1[0] + sl1[1]) + (sl1[2] + sl1[3]));
-    l2 = fmaf(a2, l2, (sl2[0] + sl2[1]) + (sl2[2] + sl2[3]));
-    acc = fmaf(a1, acc, (sa[0] + sa[1]) + (sa[2] + sa[3]));
+    const SKL_LDS char* cur = lds + buf * 2 * TILE;
+    tile_scores<T, D, NKB>(cur, cur + TILE, qf1, qf2, col, h, s1, s2);
+    if (need_mask)
+      tile_update<true, NKB>(st, s1, s2, c, k0, h, klimit, p.causal, qlim);
+    else
+      tile_update<false, NKB>(st, s1, s2, c, k0, h, klimit, p.causal, qlim);
   }
 
   // merge the two lane halves: same query, disjoint key subsets
-  const float om1 = __shfl_xor(m1, 32), ol1 = __shfl_xor(l1, 32), oacc = __shfl_xor(acc, 32);
-  const float om2 = __shfl_xor(m2, 32), ol2 = __shfl_xor(l2, 32);
-  const float M1 = fmaxf(m1, om1), M2 = fmaxf(m2, om2);
-  const float w = fast_exp2((m1 - M1) * c), ow = fast_exp2((om1 - M1) * c);
-  const float v = fast_exp2((m2 - M2) * c), ov = fast_exp2((om2 - M2) * c);
-  const float L1 = l1 * w + ol1 * ow;
-  const float ACC = acc * w + oacc * ow;
-  const float L2 = l2 * v + ol2 * ov;
+  const float om1 = __shfl_xor(st.m1, 32), ol1 = __shfl_xor(st.l1, 32), oacc = __shfl_xor(st.acc, 32);
+  const float om2 = __shfl_xor(st.m2, 32), ol2 = __shfl_xor(st.l2, 32);
+  const float M1 = fmaxf(st.m1, om1), M2 = fmaxf(st.m2, om2);
+  const float w = fast_exp2((st.m1 - M1) * c), ow = fast_exp2((om1 - M1) * c);
+  const float v = fast_exp2((st.m2 - M2) * c), ov = fast_exp2((om2 - M2) * c);
+  const float L1 = st.l1 * w + ol1 * ow;
+  const float ACC = st.acc * w + oacc * ow;
+  const float L2 = st.l2 * v + ol2 * ov;
   if (h == 0 && qrow < p.n_q) {
     if (SPLIT) {
       float* o = p.part + (((size_t)split * p.heads + head) * p.n_q + qrow) * 5;
