@@ -32,6 +32,8 @@
 //   * Causal: the key-block kernels start at the first query tile that sees
 //     their first key; tiles past a wave's frontier are skipped; only tiles
 //     crossing the diagonal or a tail take the masked path.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -187,7 +189,7 @@ struct KvCfg {
 };
 
 template <typename T, int D, int SETTING, bool FUSED>
-__global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_kv_kernel(BwdParams p) {
   using G = Geom<T, D>;
   using C = KvCfg<T, D>;
   constexpr int NW = C::NW, BT = C::BT, NQB = C::NQB, TILE = C::TILE, DB = D / 32;
@@ -262,7 +264,18 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
     issue_tile_async<T, D, BT, NW>(q2, t0 * BT, p.n_q, lds + TILE, tid, wave);
     load_coefs(t0 * BT, coef);
   }
-  for (int t = 0; t < ntiles; ++t) {
+  // Masking is needed only on tiles that cross the causal diagonal (the
+  // first tiles of this block's query range) or hold a tail (the last tile,
+  // or every tile of the last key block).  Three loops (leading masked,
+  // unmasked, trailing masked) keep one straight-line body per loop, so the
+  // compiler never holds both bodies' state at once.  Every iteration has
+  // the same barriers, so waves of one workgroup may sit in different loops.
+  auto tile_needs_mask = [&](int t) {
+    const int q0 = (t0 + t) * BT;
+    return (q0 + BT > p.n_q) || (kw0 + 32 > p.n_k) || (p.causal && kw0 + 31 > q0 + off);
+  };
+  auto tile = [&](int t, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int q0 = (t0 + t) * BT;
     const int buf = t & 1;
     const SKL_LDS char* t1 = lds + buf * 2 * TILE;
@@ -270,11 +283,15 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
     const SKL_LDS float* cf = coef + buf * 3 * BT;
     wait_async_loads();
     __syncthreads();  // tile t and its coefficients visible; tile t-1's readers done
-    if (t + 1 < ntiles) {
+    // next tile: Q rows by LDS DMA now; its coefficients into registers now
+    // and into LDS at the end of this tile, when the loads have long landed
+    const bool has_next = t + 1 < ntiles;
+    float na = 0.f, nb_ = 0.f, nc = 0.f;
+    if (has_next) {
       SKL_LDS char* nb = lds + (buf ^ 1) * 2 * TILE;
       issue_tile_async<T, D, BT, NW>(q1, q0 + BT, p.n_q, nb, tid, wave);
       issue_tile_async<T, D, BT, NW>(q2, q0 + BT, p.n_q, nb + TILE, tid, wave);
-      load_coefs(q0 + BT, coef + (buf ^ 1) * 3 * BT);
+      if (tid < BT && q0 + BT + tid < p.n_q) row_coefs<SETTING>(p, hq + q0 + BT + tid, na, nb_, nc);
     }
     const SKL_LDS char* tsrc = SETTING == 1 ? t2 : t1;   // the setting's Q
     if constexpr (!C::TR) {
@@ -283,21 +300,22 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
       });
       __syncthreads();
     }
-
     const int qlast = min(q0 + BT, p.n_q) - 1;
     const bool skip = wave_idle || (p.causal && kw0 > qlast + off);
-    const bool need_mask = (q0 + BT > p.n_q) || (kw0 + 32 > p.n_k) || (p.causal && kw0 + 31 > q0 + off);
+    if (!skip) {
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      float ds[16];
-      if (!skip) {
+      for (int qb = 0; qb < NQB; ++qb) {
         f32x16 s1 = f32x16{}, s2 = f32x16{};
+        __builtin_amdgcn_s_setprio(1);   // MFMA phase first when two waves share a SIMD
 #pragma unroll
         for (int g = 0; g < G::kGroups; ++g) {
           const int ob = lds_chunk_off<T, D>(qb * 32 + col, 2 * g + h);
           s1 = mfma_chunk<T>(*(const SKL_LDS u32x4*)(t1 + ob), kf1[g], s1);
           s2 = mfma_chunk<T>(*(const SKL_LDS u32x4*)(t2 + ob), kf2[g], s2);
         }
+        if constexpr (sizeof(T) == 2) sched_lds_mfma_pipeline<2 * G::kGroups, 2>();
+        __builtin_amdgcn_s_setprio(0);
+        float ds[16];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
           const int qi = qb * 32 + 8 * m + 4 * h;   // first of four consecutive queries
@@ -308,9 +326,9 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * m + e;
             float v = dlogit<SETTING>(s1[r], s2[r], c, ca[e], cb[e], cc[e]);
-            if (need_mask) {
+            if (MASK) {
               const int q = q0 + qi + e;
-              const bool ok = q < p.n_q && key < p.n_k && (!p.causal || key <= q + off);
+              const bool ok = (q < p.n_q) & (key < p.n_k) & ((p.causal == 0) | (key <= q + off));
               v = ok ? v : 0.f;
             }
             ds[r] = v;
@@ -324,21 +342,27 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
           else
             dkt[db] = kgroup_mfma<T>(qt + (db * 32 + col) * C::QT::kStride, qb * 32, h, ds, dkt[db]);
         }
-      } else {
+        if (FUSED) {
+          // this dS block -> LDS as [query][key]
+          const int kl = wave * 32 + col;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) ds[r] = 0.f;
+          for (int r = 0; r < 16; ++r) {
+            const int ql = qb * 32 + acc_row(r, h);
+            *(SKL_LDS T*)(dst + ql * C::DS::kStride + kl * (int)sizeof(T)) = (T)ds[r];
+          }
+        }
       }
-      if (FUSED) {
-        // this dS block -> LDS as [query][key]
-        const int kl = wave * 32 + col;
+    } else if (FUSED) {
+      // nothing to add from these keys: their dS columns are zero
+      const int kl = wave * 32 + col;
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int ql = qb * 32 + acc_row(r, h);
-          *(SKL_LDS T*)(dst + ql * C::DS::kStride + kl * (int)sizeof(T)) = (T)ds[r];
+          *(SKL_LDS T*)(dst + ql * C::DS::kStride + kl * (int)sizeof(T)) = (T)0.f;
         }
-      }
     }
-
     if (FUSED) {
       __syncthreads();
       // dQ(queries, d) = dS(queries, keys) K(keys, d) over this block's keys
@@ -360,7 +384,18 @@ __global__ __launch_bounds__(256) void bwd_kv_kernel(BwdParams p) {
         }
       }
     }
-  }
+    if (has_next && tid < BT) {
+      SKL_LDS float* cn = coef + (buf ^ 1) * 3 * BT;
+      cn[tid] = na;
+      cn[BT + tid] = nb_;
+      cn[2 * BT + tid] = nc;
+    }
+  };
+  settle_scalar_loads();
+  int t = 0;
+  for (; t < ntiles && tile_needs_mask(t); ++t) tile(t, std::true_type{});
+  for (; t < ntiles && !tile_needs_mask(t); ++t) tile(t, std::false_type{});
+  for (; t < ntiles; ++t) tile(t, std::true_type{});
 
   // dK rows of this lane's key: registers 4m..4m+3 are four consecutive d
   if (key < p.n_k) {
@@ -463,7 +498,14 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdParams p) {
     issue_tile_async<T, D, BK, NW>(k1, kbeg, p.n_k, lds, tid, wave);
     issue_tile_async<T, D, BK, NW>(k2, kbeg, p.n_k, lds + TILE, tid, wave);
   }
-  for (int t = 0; t < ntiles; ++t) {
+  // Masked tiles: the last ones (causal diagonal, key tail) or all of them
+  // (query tail); three loops as in the key-block kernel.
+  auto tile_needs_mask = [&](int t) {
+    const int k0 = kbeg + t * BK;
+    return (k0 + BK > klimit) || (qw0 + 32 > p.n_q) || (p.causal && k0 + BK - 1 > qw0 + off);
+  };
+  auto tile = [&](int t, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int buf = t & 1;
     const SKL_LDS char* t1 = lds + buf * 2 * TILE;
     const SKL_LDS char* t2 = t1 + TILE;
@@ -481,25 +523,27 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdParams p) {
       });
       __syncthreads();
     }
-    if (t >= wtiles) continue;  // wave-uniform: past this wave's frontier
+    if (t >= wtiles) return;  // wave-uniform: past this wave's frontier
     const int k0 = kbeg + t * BK;
-    const bool need_mask = (k0 + BK > klimit) || (qw0 + 32 > p.n_q) || (p.causal && k0 + BK - 1 > qw0 + off);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       f32x16 s1 = f32x16{}, s2 = f32x16{};
+      __builtin_amdgcn_s_setprio(1);   // MFMA phase first when two waves share a SIMD
 #pragma unroll
       for (int g = 0; g < G::kGroups; ++g) {
         const int ob = lds_chunk_off<T, D>(kb * 32 + col, 2 * g + h);
         s1 = mfma_chunk<T>(*(const SKL_LDS u32x4*)(t1 + ob), qf1[g], s1);
         s2 = mfma_chunk<T>(*(const SKL_LDS u32x4*)(t2 + ob), qf2[g], s2);
       }
+      if constexpr (sizeof(T) == 2) sched_lds_mfma_pipeline<2 * G::kGroups, 4>();
+      __builtin_amdgcn_s_setprio(0);
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float v = dlogit<SETTING>(s1[r], s2[r], c, ca, cb, cc);
-        if (need_mask) {
+        if (MASK) {
           const int kk = k0 + kb * 32 + acc_row(r, h);
-          const bool ok = kk < klimit && qrow < p.n_q && (!p.causal || kk <= qrow + off);
+          const bool ok = (kk < klimit) & (qrow < p.n_q) & ((p.causal == 0) | (kk <= qrow + off));
           v = ok ? v : 0.f;
         }
         ds[r] = v;
@@ -513,7 +557,12 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdParams p) {
           dqt[db] = kgroup_mfma<T>(kt + (db * 32 + col) * C::KT::kStride, kb * 32, h, ds, dqt[db]);
       }
     }
-  }
+  };
+  settle_scalar_loads();
+  int t = 0;
+  for (; t < ntiles && tile_needs_mask(t); ++t) tile(t, std::true_type{});
+  for (; t < ntiles && !tile_needs_mask(t); ++t) tile(t, std::false_type{});
+  for (; t < ntiles; ++t) tile(t, std::true_type{});
 
   if (qrow < p.n_q) {
     float* out = p.dq + (hq + qrow) * D;

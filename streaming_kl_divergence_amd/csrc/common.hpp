@@ -2,13 +2,12 @@
 //
 // Tiles of K (or Q) rows live in LDS as rows of 16-byte chunks.  A chunk's
 // slot inside its row is XOR-swizzled with a function of the row index that
-// serves both read patterns of the kernels:
+// serves both read patterns of the kernels (64 banks of 4 bytes):
 //   * MFMA operand reads (one 16-byte chunk per lane, rows r .. r+15 at the
-//     same logical chunk): the 16 rows get 16 distinct slots;
-//   * transposing reads (ds_read_b64_tr_b16: four consecutive rows, one
-//     aligned pair of chunks): the XOR keeps each pair together and moves the
-//     four rows to four distinct pairs.
-// So neither pattern conflicts on a bank.
+//     same logical chunk, 16 lanes per LDS cycle): 16 distinct banks groups;
+//   * transposing reads (ds_read_b64_tr_b16, 32 lanes per cycle: four
+//     consecutive rows times one aligned quad of chunks): the four rows land
+//     on four different quads, so the 32 lanes touch all 64 banks once.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -39,12 +38,16 @@ struct Geom {
   static_assert(kChunks >= 8, "rows must be at least 128 bytes");
 };
 
-// Swizzle of row `row`: ((row mod 8) << 1 | bit 3 of row) for rows of 16 or
-// more chunks, ((row mod 4) << 1 | bit 2 of row) for rows of 8 chunks.
+// Swizzle of row `row` (XORed into the chunk index):
+//   rows of 16+ chunks (256+ bytes, every row starts at bank 0):
+//     4 * (row mod 4) + (row / 4) mod 4   - quad index moves with row mod 4,
+//     position inside the quad with row / 4;
+//   rows of 8 chunks (128 bytes, odd rows use the other 32 banks):
+//     4 * ((row / 2) mod 2) + (row / 4) mod 4.
 template <int kChunks>
 __device__ __forceinline__ int row_swizzle(int row) {
-  if constexpr (kChunks >= 16) return ((row & 7) << 1) | ((row >> 3) & 1);
-  else return ((row & 3) << 1) | ((row >> 2) & 1);
+  if constexpr (kChunks >= 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
 // Byte offset of chunk `c` of tile row `row` inside an LDS tile.
@@ -88,6 +91,26 @@ __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 *
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// One 16-byte-per-lane copy from global memory straight into LDS
+// (global_load_lds_dwordx4): lane i's 16 bytes land at lds_base + 16 * i.
+// Written as inline assembly on purpose: when the compiler sees an LDS DMA in
+// flight it waits for every LDS read with lgkmcnt(0), which stalls each MFMA
+// for a full LDS latency.  LDS reads complete in order among themselves, so
+// waiting for "at most the reads issued after mine" is correct whether or
+// not the DMA is counted too (it can only raise the count).  Completion of
+// the DMA itself is ordered by wait_async_loads() and a barrier before any
+// wave reads the tile.  SALU writes to M0 need one wait state before an LDS
+// DMA, hence the s_nop.
+__device__ __forceinline__ void lds_dma_16(const void* src, uint32_t lds_base) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(lds_base)
+      : "memory", "m0");
+}
+
 // Issue the asynchronous copy of a [BK, D] tile (rows key0 .. key0+BK-1 of the
 // head whose row 0 is at `g`) into LDS with the swizzled layout.  Rows past
 // n_rows are clamped to the last row, so every load is in bounds; the caller
@@ -108,10 +131,32 @@ __device__ __forceinline__ void issue_tile_async(const char* __restrict__ g, int
     const int src_row = min(key0 + row, n_rows - 1);
     const char* src = g + (size_t)src_row * G::kRowBytes + c * 16;
     // lane i of this wave lands at base + 16 * i
-    __builtin_amdgcn_global_load_lds((const void*)src,
-                                     (SKL_LDS void*)(tile + (i * NW * 64 + wave * 64) * 16), 16, 0, 0);
+    lds_dma_16(src, __builtin_amdgcn_readfirstlane(
+                        (uint32_t)(uintptr_t)(tile + (i * NW * 64 + wave * 64) * 16)));
   }
 }
+
+// Scheduling pattern for a run of N MFMAs that each take one operand from
+// LDS: issue the first AHEAD reads, then alternate one MFMA with one read, so
+// AHEAD reads are always in flight and no MFMA waits a full LDS latency.
+// (Masks: 0x008 MFMA, 0x100 DS read.)
+template <int N, int AHEAD>
+__device__ __forceinline__ void sched_lds_mfma_pipeline() {
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+}
+
+// Wait for every outstanding scalar load (kernel arguments).  Scalar loads
+// complete out of order, so while one is pending the compiler can only wait
+// for LDS reads with lgkmcnt(0); after this it counts LDS reads precisely.
+__device__ __forceinline__ void settle_scalar_loads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 __device__ __forceinline__ void wait_async_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

@@ -69,7 +69,7 @@ __device__ __forceinline__ void tile_update(RowState& st, f32x16* s1, f32x16* s2
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k0 + kb * 32 + acc_row(r, h);
-        const bool ok = key < klimit && (!causal || key <= qlim);
+        const bool ok = (key < klimit) & ((causal == 0) | (key <= qlim));
         s1[kb][r] = ok ? s1[kb][r] : -INFINITY;
         s2[kb][r] = ok ? s2[kb][r] : -INFINITY;
       }
