@@ -64,15 +64,16 @@ def _as64(a) -> np.ndarray:
     return np.asarray(a, dtype=np.float64)
 
 
-def allowed_mask(rows: np.ndarray, n_q: int, n_k: int, causal: bool) -> np.ndarray:
-    """Boolean [len(rows), n_k]: which keys query row i may attend to.
+def allowed_mask(rows: np.ndarray, n_q: int, n_k: int, causal: bool, keys=None) -> np.ndarray:
+    """Boolean [len(rows), n_k] (or [len(rows), len(keys)] for a key subset):
+    which keys query row i may attend to.
 
     Non-causal: every key.  Causal (bottom-right aligned): j <= i + (n_k - n_q).
     """
     rows = np.asarray(rows, dtype=np.int64)
-    j = np.arange(n_k, dtype=np.int64)[None, :]
+    j = (np.arange(n_k, dtype=np.int64) if keys is None else np.asarray(keys, dtype=np.int64))[None, :]
     if not causal:
-        return np.ones((rows.size, n_k), dtype=bool)
+        return np.ones((rows.size, j.shape[1]), dtype=bool)
     return j <= (rows[:, None] + (n_k - n_q))
 
 
@@ -203,6 +204,37 @@ def dk_keys(setting: int, q1, k1, q2, k2, scale: float, causal: bool, keys, dkl=
         kl = _kl_of_rows(mask, lp1, lp2)
         ds = _dlogits(setting, mask, lp1, lp2, kl, g_all[r])
         out += scale * (ds[:, keys].T @ q_t[r])
+    return out
+
+
+def dk_keys_from_state(setting: int, q1, k1, q2, k2, scale: float, causal: bool, keys,
+                       lse1, lse2, kl, dkl=None):
+    """dK (of the chosen setting) for selected key rows, given every query row's
+    (LSE1, LSE2, KL) from forward_head.
+
+    Same sum as dk_keys: dK_j = scale * sum_i dS_ij q_i, with dS_ij formed from
+    the logits s_t,ij = scale q_t,i . k_t,j and the saved per-row statistics
+    (log P_t,ij = s_t,ij - LSE_t,i), as the backward of the paper's Methodology
+    ("Backward Pass": recomputation from the saved log-sum-exps) prescribes.
+    Only the selected key columns are materialised, so the cost is
+    O(N_Q * len(keys) * d) once the statistics exist.
+    """
+    q1, k1, q2, k2 = map(_as64, (q1, k1, q2, k2))
+    lse1, lse2, kl = map(_as64, (lse1, lse2, kl))
+    keys = np.asarray(keys, dtype=np.int64)
+    n_q, n_k = q1.shape[0], k1.shape[0]
+    g_all = np.ones(n_q) if dkl is None else _as64(dkl)
+    q_t = q2 if setting == 1 else q1
+    out = np.zeros((keys.size, q1.shape[1]))
+    for b in range(0, n_q, ROW_BLOCK):
+        r = np.arange(b, min(n_q, b + ROW_BLOCK))
+        mask = allowed_mask(r, n_q, n_k, causal, keys)
+        s1 = scale * (q1[r] @ k1[keys].T)
+        s2 = scale * (q2[r] @ k2[keys].T)
+        lp1 = np.where(mask, s1 - lse1[r, None], -np.inf)
+        lp2 = np.where(mask, s2 - lse2[r, None], -np.inf)
+        ds = _dlogits(setting, mask, lp1, lp2, kl[r], g_all[r])
+        out += scale * (ds.T @ q_t[r])
     return out
 
 

@@ -117,6 +117,10 @@ def pin_torch_autograd(oracle, seed=2):
             keys = np.array([0, n_k // 3, n_k - 1])
             assert np.allclose(oracle.dk_keys(setting, q1, k1, q2, k2, scale, causal, keys, g), dk[keys],
                                rtol=1e-12, atol=1e-14)
+            # dK columns from the saved per-row statistics, against torch's dK directly
+            skl, sl1, sl2 = oracle.forward_head(q1, k1, q2, k2, scale, causal)
+            dks = oracle.dk_keys_from_state(setting, q1, k1, q2, k2, scale, causal, keys, sl1, sl2, skl, g)
+            assert np.allclose(dks, tdk[keys], rtol=1e-10, atol=1e-13), (setting, np.abs(dks - tdk[keys]).max())
 
 
 # ---- P3: invariants ------------------------------------------------------------

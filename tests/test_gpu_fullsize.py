@@ -1,0 +1,197 @@
+"""Full-size workloads on the GPU against the fp64 oracle, in the launch
+configuration the benchmark times.
+
+* 64K causal (32 heads, N_Q = N_K = 65536, d = 128, bf16, correlated student):
+  forward on every row of head 0 and on sampled rows of every head (first and
+  last 256 rows, rows around query-tile boundaries, seeded random rows); both
+  backward settings through the dK-only and dQ-only launches: dQ on sampled
+  rows of heads 0 and 31, dK on sampled keys of head 0 (from the oracle's own
+  per-row statistics of that head), and on every head the identities
+  sum_j dK_j = 0 and sum_i q_i . dQ_i = sum_j k_j . dK_j.
+* 512K-key decode (32 heads, one query): split-K with the automatic split count
+  and with explicit counts, and the single-pass kernel, all heads.
+* 128K non-causal (32 heads): forward on sampled rows of every head; Setting 2
+  dQ on sampled rows of heads 0 and 31, dK on sampled keys of head 0, and the
+  identities on every head.
+
+The oracle never sees a GPU value: its inputs are the seeded generators' arrays.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from tests.gpu_util import chunks, head64, log, need_gpu, pmap, workload_device_inputs
+from tests.parity import compare
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle_forward(a, w, rows):
+    """(KL, LSE1, LSE2) of the given rows of one head, row blocks in threads."""
+    parts = pmap(lambda r: oracle.forward_head(*a, w.scale, w.causal, r), chunks(rows))
+    return tuple(np.concatenate([p[t] for p in parts]) for t in range(3))
+
+
+def _oracle_dq(a, w, setting, rows):
+    return np.concatenate(pmap(lambda r: oracle.dq_rows(setting, *a, w.scale, w.causal, r), chunks(rows)))
+
+
+def _oracle_dk(a, w, setting, keys, state):
+    """dK at sampled keys from the oracle's full per-row statistics of the head.
+    Causal: the mask depends on the absolute row, so threads split the keys;
+    non-causal: threads split the query rows and the partial sums are added."""
+    kl, l1, l2 = state
+    if w.causal:
+        parts = chunks(keys, max(1, keys.size // 8 + 1))
+        return np.concatenate(pmap(lambda k: oracle.dk_keys_from_state(setting, *a, w.scale, True, k, l1, l2, kl),
+                                   parts))
+    blocks = chunks(np.arange(a[0].shape[0]), max(256, a[0].shape[0] // 16))
+    outs = pmap(lambda r: oracle.dk_keys_from_state(setting, a[0][r], a[1], a[2][r], a[3], w.scale, False,
+                                                    keys, l1[r], l2[r], kl[r]), blocks)
+    return np.sum(outs, axis=0)
+
+
+def _sample_rows(n, rng, edge=256, boundaries=16, random=256, tile=128):
+    edge = min(edge, n)
+    b = rng.integers(1, max(2, n // tile), boundaries) * tile
+    parts = [np.arange(edge), n - 1 - np.arange(edge), b - 1, b, b + 1, rng.integers(0, n, random)]
+    r = np.unique(np.concatenate(parts))
+    return r[(r >= 0) & (r < n)]
+
+
+def _identities(q, k, dq, dk, name):
+    """sum_j dK_j = 0 per head, and sum_i q_i . dQ_i = sum_j k_j . dK_j per head
+    (both are scale * sum_ij dS_ij q_i . k_j)."""
+    import torch
+    colsum = dk.double().sum(1).abs()                       # [H, d]
+    mag = dk.double().abs().sum(1)
+    n_k = dk.shape[1]
+    assert bool((colsum <= 2e-2 * mag / np.sqrt(n_k) + 1e-6).all()), f"{name}: sum_j dK_j != 0"
+    lhs = (q.double() * dq.double()).sum((1, 2))
+    rhs = (k.double() * dk.double()).sum((1, 2))
+    ref = (q.double().abs() * dq.double().abs()).sum((1, 2))
+    bad = (lhs - rhs).abs() > 2e-3 * ref
+    assert not bool(bad.any()), f"{name}: q.dQ != k.dK on heads {torch.nonzero(bad).flatten().tolist()}"
+
+
+@pytest.fixture(scope="module")
+def causal64k():
+    need_gpu()
+    import torch
+    import streaming_kl_divergence_amd as skl
+    w = W.WORKLOADS["causal64k"]
+    log(f"case {w}: upload")
+    dev = workload_device_inputs(w)
+    q1, k1, q2, k2 = dev
+    kl, l1, l2 = skl.fwd(q1, k1, q2, k2, w.scale, w.causal)
+    assert skl.bwd_select(w.n_q, w.n_k, w.heads, w.head_dim, w.causal) == "separate"
+    grads = {}
+    for setting in (1, 2):
+        dq = torch.empty(w.heads, w.n_q, w.head_dim, device="cuda", dtype=torch.float32)
+        dk = torch.empty(w.heads, w.n_k, w.head_dim, device="cuda", dtype=torch.float32)
+        kw = dict(kl=kl) if setting == 2 else {}
+        skl.bwd(setting, q1, k1, q2, k2, w.scale, w.causal, l1, l2, path="dk_only", dk=dk, **kw)
+        skl.bwd(setting, q1, k1, q2, k2, w.scale, w.causal, l1, l2, path="dq_only", dq=dq, **kw)
+        grads[setting] = (dq, dk)
+    torch.cuda.synchronize()
+    log("causal64k: GPU done; oracle head 0 (all rows)")
+    a0 = head64(w, 0)
+    state0 = _oracle_forward(a0, w, np.arange(w.n_q))
+    log("causal64k: oracle head 0 done")
+    return w, dev, (kl, l1, l2), grads, a0, state0
+
+
+def test_causal64k_forward(causal64k):
+    w, dev, (kl, l1, l2), _, _, state0 = causal64k
+    kl, l1, l2 = [t.cpu().numpy() for t in (kl, l1, l2)]
+    rkl, rl1, rl2 = state0
+    compare(l1[0], rl1, "bf16", "h0 lse1")
+    compare(l2[0], rl2, "bf16", "h0 lse2")
+    compare(kl[0], rkl, "bf16", "h0 kl")
+    rng = np.random.default_rng(21)
+    for h in range(1, w.heads):
+        rows = _sample_rows(w.n_q, rng, edge=64, boundaries=8, random=64)
+        a = head64(w, h)
+        rkl, rl1, rl2 = _oracle_forward(a, w, rows)
+        compare(l1[h, rows], rl1, "bf16", f"h{h} lse1")
+        compare(l2[h, rows], rl2, "bf16", f"h{h} lse2")
+        compare(kl[h, rows], rkl, "bf16", f"h{h} kl")
+    log("causal64k forward: all heads checked")
+
+
+@pytest.mark.parametrize("setting", [1, 2])
+def test_causal64k_backward(causal64k, setting):
+    w, dev, _, grads, a0, state0 = causal64k
+    dq, dk = grads[setting]
+    q_t, k_t = (dev[2], dev[3]) if setting == 1 else (dev[0], dev[1])
+    _identities(q_t, k_t, dq, dk, f"causal64k setting {setting}")
+    rng = np.random.default_rng(30 + setting)
+    rows = _sample_rows(w.n_q, rng, edge=32, boundaries=4, random=64)
+    for h in (0, w.heads - 1):
+        a = a0 if h == 0 else head64(w, h)
+        rdq = _oracle_dq(a, w, setting, rows)
+        compare(dq[h, rows].cpu().numpy(), rdq, "bf16", f"setting {setting} h{h} dq")
+    keys = _sample_rows(w.n_k, rng, edge=16, boundaries=4, random=32)
+    rdk = _oracle_dk(a0, w, setting, keys, state0)
+    compare(dk[0, keys].cpu().numpy(), rdk, "bf16", f"setting {setting} h0 dk")
+    log(f"causal64k setting {setting}: checked")
+
+
+def test_decode512k_splitk():
+    """One query against 512K keys per head: split-K (automatic and explicit
+    split counts) and the single-pass kernel, all heads."""
+    need_gpu()
+    import torch
+    import streaming_kl_divergence_amd as skl
+    w = W.WORKLOADS["decode512k"]
+    log(f"case {w}")
+    q1, k1, q2, k2 = workload_device_inputs(w)
+    auto = skl.splitk_auto(w.n_q, w.n_k, w.heads, w.head_dim)
+    assert auto > 1
+    runs = {f"splitk auto={auto}": skl.fwd_splitk(q1, k1, q2, k2, w.scale, w.causal)}
+    for s in (7, 256):
+        runs[f"splitk {s}"] = skl.fwd_splitk(q1, k1, q2, k2, w.scale, w.causal, num_splits=s)
+    runs["single pass"] = skl.fwd(q1, k1, q2, k2, w.scale, w.causal)
+    torch.cuda.synchronize()
+    ref = pmap(lambda h: oracle.forward_head(*head64(w, h), w.scale, w.causal, np.array([0])), range(w.heads))
+    rkl, rl1, rl2 = (np.array([r[t][0] for r in ref]) for t in range(3))
+    for name, (kl, l1, l2) in runs.items():
+        compare(l1.cpu().numpy()[:, 0], rl1, "bf16", f"{name} lse1")
+        compare(l2.cpu().numpy()[:, 0], rl2, "bf16", f"{name} lse2")
+        compare(kl.cpu().numpy()[:, 0], rkl, "bf16", f"{name} kl")
+    log("decode512k: all heads checked")
+
+
+def test_noncausal128k_forward_setting2():
+    """128K x 128K non-causal, forward + Setting 2 backward (the selector's path)."""
+    need_gpu()
+    import torch
+    import streaming_kl_divergence_amd as skl
+    w = W.WORKLOADS["noncausal128k"]
+    log(f"case {w}: upload")
+    dev = workload_device_inputs(w)
+    q1, k1, q2, k2 = dev
+    kl, l1, l2 = skl.fwd(q1, k1, q2, k2, w.scale, w.causal)
+    dq, dk = skl.bwd(2, q1, k1, q2, k2, w.scale, w.causal, l1, l2, kl=kl)
+    torch.cuda.synchronize()
+    log("noncausal128k: GPU done")
+    _identities(q1, k1, dq, dk, "noncausal128k setting 2")
+    kl, l1, l2 = [t.cpu().numpy() for t in (kl, l1, l2)]
+    rng = np.random.default_rng(41)
+    for h in range(w.heads):
+        rows = _sample_rows(w.n_q, rng, edge=16, boundaries=4, random=16)
+        rkl, rl1, rl2 = _oracle_forward(head64(w, h), w, rows)
+        compare(l1[h, rows], rl1, "bf16", f"h{h} lse1")
+        compare(l2[h, rows], rl2, "bf16", f"h{h} lse2")
+        compare(kl[h, rows], rkl, "bf16", f"h{h} kl")
+    log("noncausal128k: forward rows checked; oracle head 0 (all rows)")
+    a0 = head64(w, 0)
+    rows = _sample_rows(w.n_q, rng, edge=16, boundaries=4, random=48)
+    for h in (0, w.heads - 1):
+        a = a0 if h == 0 else head64(w, h)
+        compare(dq[h, rows].cpu().numpy(), _oracle_dq(a, w, 2, rows), "bf16", f"h{h} dq1")
+    state0 = _oracle_forward(a0, w, np.arange(w.n_q))
+    keys = _sample_rows(w.n_k, rng, edge=16, boundaries=4, random=32)
+    compare(dk[0, keys].cpu().numpy(), _oracle_dk(a0, w, 2, keys, state0), "bf16", "h0 dk1")
+    log("noncausal128k: setting 2 checked")

@@ -48,6 +48,12 @@ MUTANTS = {
     # teacher logits built from the student's keys
     "s1_operand": ("s1 = scale * (q1[rows] @ k1.T)", "s1 = scale * (q1[rows] @ k2.T)"),
     # upstream weight ignored in Setting 2
+    # dK from saved statistics with the student's LSE in the teacher's log-probabilities
+    "state_wrong_lse": ("lp1 = np.where(mask, s1 - lse1[r, None], -np.inf)",
+                        "lp1 = np.where(mask, s1 - lse2[r, None], -np.inf)"),
+    # dK from saved statistics ignoring the causal mask
+    "state_no_mask": ("mask = allowed_mask(r, n_q, n_k, causal, keys)",
+                      "mask = allowed_mask(r, n_q, n_k, False, keys)"),
     "set2_drop_g": ("ds = g[:, None] * p1 * (r - kl[:, None])", "ds = p1 * (r - kl[:, None])"),
 }
 
