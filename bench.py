@@ -11,7 +11,21 @@ work counts only unmasked (query, key) pairs: 4 d flop each in the forward and
 8 d in each backward setting (recomputation once; the separate path's second
 recomputation is not counted).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage:
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+      the one-line benchmark of the 64K causal step (the default).
+  python bench.py --configs
+      one JSON line per workload (tiny fp32, 8K causal, 64K causal with both
+      backward paths, 512K decode split-K vs single pass, 128K non-causal,
+      512 x 128K fused vs separate): median and min of timed runs per call.
+  python bench.py --copy-calibration ...
+      also runs one plain 1 GiB device copy first, so that a rocprofv3 --pmc
+      run sees FETCH_SIZE / WRITE_SIZE of a copy of known size.
+  python bench.py --pmc-summary FETCH_DIR WRITE_DIR
+      reads two rocprofv3 --pmc outputs (FETCH_SIZE, then WRITE_SIZE, both of a
+      --copy-calibration run), scales each counter by what it reads for the
+      1 GiB copy, and writes profiles/traffic.json (HBM bytes per launch per
+      kernel, tagged with a hash of the kernel sources).
 """
 from __future__ import annotations
 
@@ -72,6 +86,151 @@ def measured_traffic(kernel: str):
     return e.get("bytes_per_launch")
 
 
+def kernel_label(symbol: str):
+    """Benchmark label of a library kernel symbol (None for other kernels)."""
+    import re
+    m = re.match(r"_ZN3skl(\d+)(fwd_kernel|bwd_kv_kernel|bwd_q_kernel|splitk_combine_kernel)(.*)$", symbol)
+    if not m:
+        return None
+    name, targs = m.group(2), m.group(3)
+    if name in ("fwd_kernel", "splitk_combine_kernel"):
+        return name
+    st = re.search(r"Li\d+ELi(\d)ELb(\d)", targs)
+    setting, flag = (st.group(1), st.group(2)) if st else ("?", "0")
+    fused = name == "bwd_kv_kernel" and flag == "1"
+    return f"{name}{' fused' if fused else ''} set{setting}"
+
+
+COPY_BYTES = 1 << 30
+
+
+def pmc_summary(fetch_dir: str, write_dir: str):
+    """HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by the ratio of the 1 GiB copy's true bytes to what the
+    counter reads for it."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not f:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        vals = {}
+        for r in csv.DictReader(open(f[0])):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Kernel_Name"], r.get("Dispatch_Id", r.get("Correlation_Id", "")))
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"]) * 1024.0
+        out = {}
+        for (name, _), v in vals.items():
+            out.setdefault(name, []).append(v)
+        return out
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    copy = [k for k in fetch if "copyBuffer" in k or "copy" in k.lower()]
+    if not copy:
+        raise SystemExit("no copy kernel in the counter run (use --copy-calibration)")
+    ck = max(copy, key=lambda k: max(fetch[k]))
+    f_factor = COPY_BYTES / max(fetch[ck])
+    w_factor = COPY_BYTES / max(write[ck])
+    h = kernel_source_hash()
+    table = {"_calibration": {"copy_kernel": ck, "copy_bytes": COPY_BYTES, "fetch_factor": round(f_factor, 4),
+                              "write_factor": round(w_factor, 4)}}
+    for name, v in fetch.items():
+        label = kernel_label(name)
+        if label is None:
+            continue
+        fb = f_factor * float(np.mean(v))
+        wb = w_factor * float(np.mean(write.get(name, [0.0])))
+        table[label] = {"symbol": name, "dispatches": len(v), "fetch_bytes": round(fb), "write_bytes": round(wb),
+                        "bytes_per_launch": round(fb + wb), "source_hash": h}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    json.dump(table, open(path, "w"), indent=1, sort_keys=True)
+    print(json.dumps(table, indent=1, sort_keys=True))
+
+
+def _timed(fn, stream, warmup: int, reps: int):
+    """fn() enqueues work on stream; returns per-run ms from HIP events."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in evs])
+
+
+def configs_mode():
+    """One JSON line per workload: median / min ms of each call, algorithmic
+    TFLOP/s (MFMA-bound calls) or GB/s (the HBM-bound decode)."""
+    import torch
+    import streaming_kl_divergence_amd as skl
+    stream = torch.cuda.current_stream()
+    threads = min(16, os.cpu_count() or 1)
+
+    def line(w, rows, extra=None):
+        out = {"workload": w.name, "heads": w.heads, "n_q": w.n_q, "n_k": w.n_k, "head_dim": w.head_dim,
+               "dtype": w.dtype, "causal": w.causal, "elements": w.elements(), "calls": rows}
+        if extra:
+            out.update(extra)
+        print(json.dumps(out), flush=True)
+
+    def entry(ms, flop=None, hbm=None):
+        e = {"median_ms": round(float(np.median(ms)), 4), "min_ms": round(float(ms.min()), 4), "runs": len(ms)}
+        if flop:
+            tf = flop / (np.median(ms) * 1e-3) / 1e12
+            e.update({"tflops": round(float(tf), 1), "pct_peak": round(100 * float(tf) / PEAK_BF16_TFLOPS, 1)})
+        if hbm:
+            gbs = hbm / (np.median(ms) * 1e-3) / 1e9
+            e.update({"gbs": round(float(gbs), 1), "pct_hbm": round(100 * float(gbs) / PEAK_HBM_GBS, 1)})
+        return e
+
+    def run(name, settings, paths=("auto",), reps=10):
+        w = W.WORKLOADS[name]
+        q1, k1, q2, k2 = upload(w, threads)
+        d, E = w.head_dim, w.elements()
+        kl, l1, l2 = skl.fwd(q1, k1, q2, k2, w.scale, w.causal)
+        rows = {"fwd": entry(_timed(lambda: skl.fwd(q1, k1, q2, k2, w.scale, w.causal), stream, 3, reps),
+                             4 * d * E)}
+        dq = torch.empty(w.heads, w.n_q, d, device="cuda", dtype=torch.float32)
+        dk = torch.empty(w.heads, w.n_k, d, device="cuda", dtype=torch.float32)
+        for st in settings:
+            kw = dict(kl=kl) if st == 2 else {}
+            for path in paths:
+                chosen = skl.bwd_select(w.n_q, w.n_k, w.heads, d, w.causal) if path == "auto" else path
+                ms = _timed(lambda: skl.bwd(st, q1, k1, q2, k2, w.scale, w.causal, l1, l2, path=path,
+                                            dq=dq, dk=dk, **kw), stream, 3, reps)
+                rows[f"bwd set{st} {path}" + (f" ({chosen})" if path == "auto" else "")] = entry(ms, 8 * d * E)
+        line(w, rows)
+        del q1, k1, q2, k2, dq, dk
+        torch.cuda.empty_cache()
+
+    run("tiny", (1, 2))
+    run("causal8k", (1,))
+    run("causal64k", (1, 2), paths=("auto", "fused", "separate"), reps=5)
+    # decode: the same fused key loop with one split vs split-K
+    w = W.WORKLOADS["decode512k"]
+    q1, k1, q2, k2 = upload(w, threads)
+    hbm = 2 * w.heads * w.n_k * w.head_dim * 2 + 2 * w.heads * w.n_q * w.head_dim * 2 + 3 * w.heads * w.n_q * 4
+    auto = skl.splitk_auto(w.n_q, w.n_k, w.heads, w.head_dim)
+    rows = {"single pass": entry(_timed(lambda: skl.fwd(q1, k1, q2, k2, w.scale, w.causal), stream, 3, 10),
+                                 hbm=hbm)}
+    for s_ in (1, auto):
+        rows[f"splitk {s_}{' (auto)' if s_ == auto else ''}"] = entry(
+            _timed(lambda: skl.fwd_splitk(q1, k1, q2, k2, w.scale, w.causal, num_splits=s_), stream, 3, 10),
+            hbm=hbm)
+    line(w, rows, {"hbm_bytes": hbm})
+    del q1, k1, q2, k2
+    torch.cuda.empty_cache()
+    run("noncausal128k", (2,), reps=3)
+    run("smallq128k", (2,), paths=("auto", "fused", "separate"))
+
+
 def cpu_baseline():
     """The fp64 oracle, as it stands, on a bounded sample of the same workload:
     head 0 of the 64K causal workload restricted to its first 16384 queries and
@@ -105,16 +264,31 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="causal64k")
+    ap.add_argument("--configs", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(heads would shard across GPUs with no exchange; see DESIGN.md).", file=sys.stderr)
+              "(heads would shard across GPUs with no exchange between them).", file=sys.stderr)
         sys.exit(1)
 
     import torch
     import streaming_kl_divergence_amd as skl
 
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, device="cuda", dtype=torch.float32)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.configs:
+        configs_mode()
+        return
     w = W.WORKLOADS[args.workload]
     threads = min(16, os.cpu_count() or 1)
     t_up = time.perf_counter()
