@@ -147,26 +147,45 @@ __device__ __forceinline__ f32x16 kgroup_mfma_tr(const SKL_LDS char* tile, int r
 // Setting 1: (LSE1 log2e, LSE2 log2e, g)            dS = g (2^(x2 c - b) - 2^(x1 c - a))
 // Setting 2: (LSE1 log2e, g scale, -g (LSE1 - LSE2 + KL))
 //                                                 dS = 2^(x1 c - a) (b (x1 - x2) + c3)
-template <int SETTING>
-__device__ __forceinline__ void row_coefs(const BwdParams& p, size_t row, float& a, float& b, float& c3) {
-  const float g = p.dkl ? p.dkl[row] : 1.f;
-  const float l1 = p.lse1[row], l2 = p.lse2[row];
-  a = l1 * kLog2e;
-  if (SETTING == 1) {
-    b = l2 * kLog2e;
-    c3 = g;
-  } else {
-    b = g * p.scale;
-    c3 = -g * (l1 - l2 + p.kl[row]);
+// HAS_G false: no upstream weights (g = 1), so Setting 1 needs no factor and
+// Setting 2's b is the scale itself; only two per-row values vary.
+// The saved per-row values are loaded raw and turned into coefficients only
+// when needed: a load whose value is used at once makes the compiler wait for
+// it, and that wait also covers any tile DMA issued just before it.
+template <int SETTING, bool HAS_G>
+struct RowVals {
+  float l1 = 0.f, l2 = 0.f, kl = 0.f, g = 1.f;
+  __device__ __forceinline__ void load(const BwdParams& p, size_t row) {
+    l1 = p.lse1[row];
+    l2 = p.lse2[row];
+    if (SETTING == 2) kl = p.kl[row];
+    if (HAS_G) g = p.dkl[row];
   }
+  __device__ __forceinline__ void coefs(const BwdParams& p, float& a, float& b, float& c3) const {
+    a = l1 * kLog2e;
+    if (SETTING == 1) {
+      b = l2 * kLog2e;
+      c3 = g;
+    } else {
+      b = g * p.scale;
+      c3 = -g * (l1 - l2 + kl);
+    }
+  }
+};
+
+template <int SETTING, bool HAS_G>
+__device__ __forceinline__ void row_coefs(const BwdParams& p, size_t row, float& a, float& b, float& c3) {
+  RowVals<SETTING, HAS_G> v;
+  v.load(p, row);
+  v.coefs(p, a, b, c3);
 }
 
-template <int SETTING>
+template <int SETTING, bool HAS_G>
 __device__ __forceinline__ float dlogit(float x1, float x2, float c, float a, float b, float c3) {
   const float p1 = fast_exp2(fmaf(x1, c, -a));
   if (SETTING == 1) {
     const float p2 = fast_exp2(fmaf(x2, c, -b));
-    return c3 * (p2 - p1);
+    return HAS_G ? c3 * (p2 - p1) : p2 - p1;
   }
   return p1 * fmaf(b, x1 - x2, c3);
 }
@@ -188,7 +207,7 @@ struct KvCfg {
   static constexpr int kLdsFused = kLdsBase + KT::kBytes + DS::kBytes;
 };
 
-template <typename T, int D, int SETTING, bool FUSED>
+template <typename T, int D, int SETTING, bool FUSED, bool HAS_G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_kv_kernel(BwdParams p) {
   using G = Geom<T, D>;
   using C = KvCfg<T, D>;
@@ -253,16 +272,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   auto load_coefs = [&](int q0, SKL_LDS float* cf) {
     if (tid < BT) {
       float a = 0.f, b = 0.f, c3 = 0.f;
-      if (q0 + tid < p.n_q) row_coefs<SETTING>(p, hq + q0 + tid, a, b, c3);
+      if (q0 + tid < p.n_q) row_coefs<SETTING, HAS_G>(p, hq + q0 + tid, a, b, c3);
       cf[tid] = a;
       cf[BT + tid] = b;
       cf[2 * BT + tid] = c3;
     }
   };
+  TileStream<T, D, BT, NW> ts;
+  ts.init(tid);
+  // Per-row coefficients run one tile ahead of use: the raw values of tile
+  // t+1 are loaded into registers during tile t-1 and written to LDS right
+  // after the barrier that opens tile t (by then the loop-top wait has seen
+  // them land, so no wait ever covers a tile DMA in flight); the barrier that
+  // opens tile t+1 publishes them.
+  RowVals<SETTING, HAS_G> nv;
+  bool nv_ok = false;
   if (ntiles > 0) {
     issue_tile_async<T, D, BT, NW>(q1, t0 * BT, p.n_q, lds, tid, wave);
     issue_tile_async<T, D, BT, NW>(q2, t0 * BT, p.n_q, lds + TILE, tid, wave);
     load_coefs(t0 * BT, coef);
+    nv_ok = ntiles > 1 && tid < BT && (t0 + 1) * BT + tid < p.n_q;
+    if (nv_ok) nv.load(p, hq + (t0 + 1) * BT + tid);
   }
   // Masking is needed only on tiles that cross the causal diagonal (the
   // first tiles of this block's query range) or hold a tail (the last tile,
@@ -283,16 +313,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const SKL_LDS float* cf = coef + buf * 3 * BT;
     wait_async_loads();
     __syncthreads();  // tile t and its coefficients visible; tile t-1's readers done
-    // next tile: Q rows by LDS DMA now; its coefficients into registers now
-    // and into LDS at the end of this tile, when the loads have long landed
     const bool has_next = t + 1 < ntiles;
-    float na = 0.f, nb_ = 0.f, nc = 0.f;
-    if (has_next) {
-      SKL_LDS char* nb = lds + (buf ^ 1) * 2 * TILE;
-      issue_tile_async<T, D, BT, NW>(q1, q0 + BT, p.n_q, nb, tid, wave);
-      issue_tile_async<T, D, BT, NW>(q2, q0 + BT, p.n_q, nb + TILE, tid, wave);
-      if (tid < BT && q0 + BT + tid < p.n_q) row_coefs<SETTING>(p, hq + q0 + BT + tid, na, nb_, nc);
+    if (has_next && tid < BT) {
+      // tile t+1's coefficients into the buffer tile t-1 used
+      float na = 0.f, nb_ = 0.f, nc = 0.f;
+      if (nv_ok) nv.coefs(p, na, nb_, nc);
+      SKL_LDS float* cn = coef + (buf ^ 1) * 3 * BT;
+      cn[tid] = na;
+      cn[BT + tid] = nb_;
+      cn[2 * BT + tid] = nc;
     }
+    if (has_next) {
+      // tile t+1's Q rows by LDS DMA; tile t+2's raw row values into registers
+      SKL_LDS char* nb = lds + (buf ^ 1) * 2 * TILE;
+      ts.issue(q1, q0 + BT, p.n_q, nb, tid, wave);
+      ts.issue(q2, q0 + BT, p.n_q, nb + TILE, tid, wave);
+    }
+    nv_ok = t + 2 < ntiles && tid < BT && q0 + 2 * BT + tid < p.n_q;
+    if (nv_ok) nv.load(p, hq + q0 + 2 * BT + tid);
     const SKL_LDS char* tsrc = SETTING == 1 ? t2 : t1;   // the setting's Q
     if constexpr (!C::TR) {
       build_transposed<T, D, BT, 8, NW * 64>(qt, tid, [&](int r, int cc) {
@@ -320,12 +358,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int m = 0; m < 4; ++m) {
           const int qi = qb * 32 + 8 * m + 4 * h;   // first of four consecutive queries
           const f32x4 ca = *(const SKL_LDS f32x4*)(cf + qi);
-          const f32x4 cb = *(const SKL_LDS f32x4*)(cf + BT + qi);
-          const f32x4 cc = *(const SKL_LDS f32x4*)(cf + 2 * BT + qi);
+          f32x4 cb, cc;
+          if constexpr (SETTING == 1 || HAS_G)
+            cb = *(const SKL_LDS f32x4*)(cf + BT + qi);
+          else
+            cb = f32x4{p.scale, p.scale, p.scale, p.scale};
+          if constexpr (SETTING == 2 || HAS_G)
+            cc = *(const SKL_LDS f32x4*)(cf + 2 * BT + qi);
+          else
+            cc = f32x4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * m + e;
-            float v = dlogit<SETTING>(s1[r], s2[r], c, ca[e], cb[e], cc[e]);
+            float v = dlogit<SETTING, HAS_G>(s1[r], s2[r], c, ca[e], cb[e], cc[e]);
             if (MASK) {
               const int q = q0 + qi + e;
               const bool ok = (q < p.n_q) & (key < p.n_k) & ((p.causal == 0) | (key <= q + off));
@@ -384,12 +429,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
       }
     }
-    if (has_next && tid < BT) {
-      SKL_LDS float* cn = coef + (buf ^ 1) * 3 * BT;
-      cn[tid] = na;
-      cn[BT + tid] = nb_;
-      cn[2 * BT + tid] = nc;
-    }
   };
   settle_scalar_loads();
   int t = 0;
@@ -424,7 +463,7 @@ struct QCfg {
   static constexpr int kLds = 4 * TILE + (TR ? 0 : KT::kBytes);
 };
 
-template <typename T, int D, int SETTING, bool SPLIT>
+template <typename T, int D, int SETTING, bool SPLIT, bool HAS_G>
 __global__ __launch_bounds__(256) void bwd_q_kernel(BwdParams p) {
   using G = Geom<T, D>;
   using C = QCfg<T, D>;
@@ -488,12 +527,14 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdParams p) {
     }
   }
   float ca, cb, cc;
-  row_coefs<SETTING>(p, hq + qr, ca, cb, cc);
+  row_coefs<SETTING, HAS_G>(p, hq + qr, ca, cb, cc);
 
   f32x16 dqt[DB];
 #pragma unroll
   for (int i = 0; i < DB; ++i) dqt[i] = f32x16{};
 
+  TileStream<T, D, BK, NW> ts;
+  ts.init(tid);
   if (ntiles > 0) {
     issue_tile_async<T, D, BK, NW>(k1, kbeg, p.n_k, lds, tid, wave);
     issue_tile_async<T, D, BK, NW>(k2, kbeg, p.n_k, lds + TILE, tid, wave);
@@ -513,8 +554,8 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdParams p) {
     __syncthreads();
     if (t + 1 < ntiles) {
       SKL_LDS char* nb = lds + (buf ^ 1) * 2 * TILE;
-      issue_tile_async<T, D, BK, NW>(k1, kbeg + (t + 1) * BK, p.n_k, nb, tid, wave);
-      issue_tile_async<T, D, BK, NW>(k2, kbeg + (t + 1) * BK, p.n_k, nb + TILE, tid, wave);
+      ts.issue(k1, kbeg + (t + 1) * BK, p.n_k, nb, tid, wave);
+      ts.issue(k2, kbeg + (t + 1) * BK, p.n_k, nb + TILE, tid, wave);
     }
     const SKL_LDS char* tsrc = SETTING == 1 ? t2 : t1;   // the setting's K
     if constexpr (!C::TR) {
@@ -540,7 +581,7 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdParams p) {
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float v = dlogit<SETTING>(s1[r], s2[r], c, ca, cb, cc);
+        float v = dlogit<SETTING, HAS_G>(s1[r], s2[r], c, ca, cb, cc);
         if (MASK) {
           const int kk = k0 + kb * 32 + acc_row(r, h);
           const bool ok = (kk < klimit) & (qrow < p.n_q) & ((p.causal == 0) | (kk <= qrow + off));
@@ -596,14 +637,14 @@ static hipError_t zero_fill(float* p, size_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T, int D, int SETTING>
+template <typename T, int D, int SETTING, bool HAS_G>
 static hipError_t sep(const BwdParams& p, bool do_dk, bool do_dq, hipStream_t s) {
   using KC = KvCfg<T, D>;
   using QC = QCfg<T, D>;
   hipError_t e = hipSuccess;
   if (do_dk) {
     const int nkb = (p.n_k + KC::BKW - 1) / KC::BKW;
-    hipLaunchKernelGGL((bwd_kv_kernel<T, D, SETTING, false>), dim3(p.heads * nkb), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_kv_kernel<T, D, SETTING, false, HAS_G>), dim3(p.heads * nkb), dim3(256), 0, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -612,20 +653,21 @@ static hipError_t sep(const BwdParams& p, bool do_dk, bool do_dq, hipStream_t s)
   if (p.dq_splits > 1) {
     e = zero_fill(p.dq, (size_t)p.heads * p.n_q * D, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_q_kernel<T, D, SETTING, true>), dim3(p.heads * nqb * p.dq_splits), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_q_kernel<T, D, SETTING, true, HAS_G>), dim3(p.heads * nqb * p.dq_splits), dim3(256), 0, s,
+                       p);
   } else {
-    hipLaunchKernelGGL((bwd_q_kernel<T, D, SETTING, false>), dim3(p.heads * nqb), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_q_kernel<T, D, SETTING, false, HAS_G>), dim3(p.heads * nqb), dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }
 
-template <typename T, int D, int SETTING>
+template <typename T, int D, int SETTING, bool HAS_G>
 static hipError_t fused(const BwdParams& p, hipStream_t s) {
   using KC = KvCfg<T, D>;
   hipError_t e = zero_fill(p.dq, (size_t)p.heads * p.n_q * D, s);
   if (e != hipSuccess) return e;
   const int nkb = (p.n_k + KC::BKW - 1) / KC::BKW;
-  hipLaunchKernelGGL((bwd_kv_kernel<T, D, SETTING, true>), dim3(p.heads * nkb), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((bwd_kv_kernel<T, D, SETTING, true, HAS_G>), dim3(p.heads * nkb), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -642,7 +684,9 @@ static hipError_t dispatch(const BwdParams& p, int dtype, int head_dim, int mode
 template <typename T, int D, int S>
 struct SepRun {
   static hipError_t run(const BwdParams& p, int mode, hipStream_t s) {
-    return sep<T, D, S>(p, (mode & 1) != 0, (mode & 2) != 0, s);
+    // with no upstream weights the kernels skip the per-row factor g
+    if (p.dkl) return sep<T, D, S, true>(p, (mode & 1) != 0, (mode & 2) != 0, s);
+    return sep<T, D, S, false>(p, (mode & 1) != 0, (mode & 2) != 0, s);
   }
 };
 template <typename T, int D, int S>
@@ -651,7 +695,7 @@ struct FusedRun {
     if constexpr (KvCfg<T, D>::kLdsFused > 160 * 1024) {
       return hipErrorNotSupported;
     } else {
-      return fused<T, D, S>(p, s);
+      return p.dkl ? fused<T, D, S, true>(p, s) : fused<T, D, S, false>(p, s);
     }
   }
 };

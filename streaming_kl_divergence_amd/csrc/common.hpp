@@ -136,6 +136,67 @@ __device__ __forceinline__ void issue_tile_async(const char* __restrict__ g, int
   }
 }
 
+// The same copy in scalar-base form: a wave-uniform 64-bit base (SGPRs) plus a
+// 32-bit per-lane byte offset, so a tile that needs no clamping costs no
+// per-lane 64-bit address arithmetic.
+__device__ __forceinline__ void lds_dma_16_sbase(const char* base, uint32_t voff, uint32_t lds_base) {
+  // the base is wave-uniform by construction; make that visible to the
+  // compiler so it stays in SGPRs
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const char* sbase = (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds_base)
+      : "memory", "m0");
+}
+
+// Streams [BK, D] tiles of one head's rows into swizzled LDS tiles.  Each
+// lane's source offset inside a tile is fixed for the whole kernel, so it is
+// computed once; a full tile is then one scalar base per instruction.  A tile
+// that reaches past n_rows (the last one) takes the clamped path.
+template <typename T, int D, int BK, int NW>
+struct TileStream {
+  using G = Geom<T, D>;
+  static constexpr int kSlots = BK * G::kChunks;
+  static_assert(kSlots % (NW * 64) == 0, "tile must split evenly over the workgroup");
+  static constexpr int kPer = kSlots / (NW * 64);
+  static constexpr int kRowsPerInst = NW * 64 / G::kChunks;
+  // the swizzle repeats every 16 rows, so when every instruction covers a
+  // multiple of 16 rows all instructions share one lane offset
+  static constexpr bool kPeriodic = kRowsPerInst % 16 == 0;
+  uint32_t voff0;
+
+  __device__ __forceinline__ static uint32_t lane_off(int i, int tid) {
+    const int slot = i * NW * 64 + tid;
+    const int row = slot / G::kChunks;
+    const int c = (slot % G::kChunks) ^ row_swizzle<G::kChunks>(row);
+    return (uint32_t)(row * G::kRowBytes + c * 16);
+  }
+  __device__ __forceinline__ void init(int tid) { voff0 = lane_off(0, tid); }
+
+  __device__ __forceinline__ void issue(const char* __restrict__ g, int key0, int n_rows, SKL_LDS char* tile,
+                                        int tid, int wave) const {
+    if (key0 + BK > n_rows) {
+      issue_tile_async<T, D, BK, NW>(g, key0, n_rows, tile, tid, wave);
+      return;
+    }
+    const char* base = g + (size_t)key0 * G::kRowBytes;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const uint32_t lb = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(tile + (i * NW * 64 + wave * 64) * 16));
+      if constexpr (kPeriodic)
+        lds_dma_16_sbase(base + i * kRowsPerInst * G::kRowBytes, voff0, lb);
+      else
+        lds_dma_16_sbase(base, lane_off(i, tid), lb);
+    }
+  }
+};
+
 // Scheduling pattern for a run of N MFMAs that each take one operand from
 // LDS: issue the first AHEAD reads, then alternate one MFMA with one read, so
 // AHEAD reads are always in flight and no MFMA waits a full LDS latency.
@@ -158,7 +219,15 @@ __device__ __forceinline__ void sched_lds_mfma_pipeline() {
 // for LDS reads with lgkmcnt(0); after this it counts LDS reads precisely.
 __device__ __forceinline__ void settle_scalar_loads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-__device__ __forceinline__ void wait_async_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait for every outstanding vector-memory load, the LDS DMAs included.  This
+// is the s_waitcnt builtin (vmcnt 0, other counters untouched; gfx9 encoding)
+// rather than inline assembly on purpose: the compiler then knows that every
+// earlier load has landed.  Without that it keeps waits for the register
+// fragments loaded before the tile loop inside the loop, and since the
+// hardware counter also holds the DMA of the next tile (issued by inline
+// assembly the compiler cannot see), those waits stall every tile until its
+// prefetch has arrived.
+__device__ __forceinline__ void wait_async_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Transposing LDS read (bf16 tiles): lane l of each 16-lane group passes the
 // address of element (r0 + (l % 16) / 4, c0 + 4 * (l % 4)) of a row-major

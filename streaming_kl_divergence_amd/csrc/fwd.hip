@@ -185,6 +185,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
 
   // Two waves per SIMD (223 VGPRs) overlap one wave's MFMAs with the other's VALU.
   f32x16 s1[NKB], s2[NKB];
+  TileStream<T, D, BK, NW> ts;
+  ts.init(tid);
   if (ntiles > 0) {
     issue_tile_async<T, D, BK, NW>(k1, kbeg, p.n_k, lds, tid, wave);
     issue_tile_async<T, D, BK, NW>(k2, kbeg, p.n_k, lds + TILE, tid, wave);
@@ -195,8 +197,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
     const int buf = t & 1;
     if (t + 1 < ntiles) {
       SKL_LDS char* nb = lds + (buf ^ 1) * 2 * TILE;
-      issue_tile_async<T, D, BK, NW>(k1, kbeg + (t + 1) * BK, p.n_k, nb, tid, wave);
-      issue_tile_async<T, D, BK, NW>(k2, kbeg + (t + 1) * BK, p.n_k, nb + TILE, tid, wave);
+      ts.issue(k1, kbeg + (t + 1) * BK, p.n_k, nb, tid, wave);
+      ts.issue(k2, kbeg + (t + 1) * BK, p.n_k, nb + TILE, tid, wave);
     }
     if (t >= wtiles) continue;
     const int k0 = kbeg + t * BK;
