@@ -351,7 +351,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
           s1 = mfma_chunk<T>(*(const SKL_LDS u32x4*)(t1 + ob), kf1[g], s1);
           s2 = mfma_chunk<T>(*(const SKL_LDS u32x4*)(t2 + ob), kf2[g], s2);
         }
-        if constexpr (sizeof(T) == 2) sched_lds_mfma_pipeline<2 * G::kGroups, 2>();
+        if constexpr (sizeof(T) == 2) sched_lds_mfma_pipeline<2 * G::kGroups, 4>();
         __builtin_amdgcn_s_setprio(0);
         float ds[16];
 #pragma unroll

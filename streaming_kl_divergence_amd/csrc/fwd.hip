@@ -112,6 +112,60 @@ __device__ __forceinline__ void tile_update(RowState& st, f32x16* s1, f32x16* s2
   st.acc = fmaf(a1, st.acc, (sa[0] + sa[1]) + (sa[2] + sa[3]));
 }
 
+// Unmasked tile folded against the current offsets m1, m2, without this
+// tile's maxima.  The sums are scale-free, so any offset gives the same
+// result as long as no term overflows: the fold is accepted when every lane's
+// tile sum of 2^(x c - m c) stays below 2^64 (no score more than ~64 binary
+// orders above its offset), and otherwise the whole wave raises its offsets
+// to the tile maxima (rescaling l and acc, exactly the online update of the
+// pages' Methodology 1) and folds again, which cannot overflow.  An offset
+// never exceeds the true running maximum, so nothing underflows that the
+// exact update would keep.  The first tile of a lane always takes the raise
+// (its offset is the initial -1e30).  Saves the per-tile max reduction.
+template <int NKB>
+__device__ __forceinline__ bool tile_fold_at_offsets(RowState& st, const f32x16* s1, const f32x16* s2, float c) {
+  const float mc1 = st.m1 * c, mc2 = st.m2 * c;
+  float sl1[4] = {0.f, 0.f, 0.f, 0.f}, sl2[4] = {0.f, 0.f, 0.f, 0.f}, sa[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float x1 = s1[kb][r], x2 = s2[kb][r];
+      const int j = r & 3;
+      const float e1 = fast_exp2(fmaf(x1, c, -mc1));
+      sl1[j] += e1;
+      sl2[j] += fast_exp2(fmaf(x2, c, -mc2));
+      sa[j] = fmaf(e1, x1 - x2, sa[j]);
+    }
+  const float t1 = (sl1[0] + sl1[1]) + (sl1[2] + sl1[3]);
+  const float t2 = (sl2[0] + sl2[1]) + (sl2[2] + sl2[3]);
+  const bool fits = (t1 < 0x1p64f) & (t2 < 0x1p64f);   // false for inf and NaN too
+  if (__builtin_amdgcn_ballot_w64(!fits) != 0) return false;
+  st.l1 += t1;
+  st.l2 += t2;
+  st.acc += (sa[0] + sa[1]) + (sa[2] + sa[3]);
+  return true;
+}
+
+template <int NKB>
+__device__ __forceinline__ void raise_offsets(RowState& st, const f32x16* s1, const f32x16* s2, float c) {
+  float tm1 = -INFINITY, tm2 = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      tm1 = fmaxf(tm1, s1[kb][r]);
+      tm2 = fmaxf(tm2, s2[kb][r]);
+    }
+  const float n1 = fmaxf(st.m1, tm1), n2 = fmaxf(st.m2, tm2);
+  const float a1 = fast_exp2((st.m1 - n1) * c), a2 = fast_exp2((st.m2 - n2) * c);
+  st.m1 = n1;
+  st.m2 = n2;
+  st.l1 *= a1;
+  st.acc *= a1;
+  st.l2 *= a2;
+}
+
 template <typename T, int D, int NW, bool SPLIT>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   using G = Geom<T, D>;
@@ -204,11 +258,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
     const int k0 = kbeg + t * BK;
     const bool need_mask = (k0 + BK > klimit) || (p.causal && k0 + BK - 1 > qw0 + off);
     const SKL_LDS char* cur = lds + buf * 2 * TILE;
+    __builtin_amdgcn_s_setprio(1);   // MFMA phase first when two waves share a SIMD
     tile_scores<T, D, NKB>(cur, cur + TILE, qf1, qf2, col, h, s1, s2);
-    if (need_mask)
+    __builtin_amdgcn_s_setprio(0);
+    if (need_mask) {
       tile_update<true, NKB>(st, s1, s2, c, k0, h, klimit, p.causal, qlim);
-    else
-      tile_update<false, NKB>(st, s1, s2, c, k0, h, klimit, p.causal, qlim);
+    } else if (!tile_fold_at_offsets<NKB>(st, s1, s2, c)) {
+      raise_offsets<NKB>(st, s1, s2, c);
+      tile_fold_at_offsets<NKB>(st, s1, s2, c);
+    }
   }
 
   // merge the two lane halves: same query, disjoint key subsets
