@@ -80,6 +80,35 @@ def test_edge_shapes(idx):
     _check_all_rows(arrs, dtype, sm / np.sqrt(d), causal, name=str(case))
 
 
+def _drift_case(seed, heads, n_q, n_k, d, rising: bool):
+    """Logits that drift along the keys by about 256 binary orders over a row
+    (queries near 8u, keys near ramp_j * u for a random unit u): rising, every
+    few tiles a score exceeds the running offset by more than 2^64, so the
+    forward must raise its offsets mid-row; falling, later tiles underflow."""
+    rng = np.random.default_rng(seed)
+    d_ = np.float32
+    arrs = [np.empty((heads, n, d), dtype=np.float32) for n in (n_q, n_k, n_q, n_k)]
+    for h in range(heads):
+        u = rng.standard_normal(d).astype(d_)
+        u /= np.linalg.norm(u)
+        t = np.arange(n_k, dtype=d_) / n_k
+        ramp = d_(251.0) * (t if rising else 1 - t)
+        q1 = 8 * u + d_(0.5) * rng.standard_normal((n_q, d), dtype=d_)
+        k1 = ramp[:, None] * u + d_(0.5) * rng.standard_normal((n_k, d), dtype=d_)
+        arrs[0][h], arrs[1][h] = q1, k1
+        arrs[2][h] = q1 + d_(0.3) * rng.standard_normal((n_q, d), dtype=d_)
+        arrs[3][h] = k1 + d_(0.3) * rng.standard_normal((n_k, d), dtype=d_)
+    return [W.round_bf16(a) for a in arrs]
+
+
+@pytest.mark.parametrize("rising,causal", [(True, False), (True, True), (False, True)])
+def test_drifting_logits(rising, causal):
+    need_gpu()
+    log(f"case drifting logits rising={rising} causal={causal}")
+    arrs = _drift_case(14 + 2 * rising + causal, 2, 96, 2048, 128, rising)
+    _check_all_rows(arrs, "bf16", 1 / np.sqrt(128), causal, name=f"drift rising={rising} causal={causal}")
+
+
 @pytest.mark.parametrize("splits", [1, 2, 7, 0])
 def test_splitk_matches_oracle(splits):
     need_gpu()
