@@ -18,6 +18,11 @@ Usage:
       one JSON line per workload (tiny fp32, 8K causal, 64K causal with both
       backward paths, 512K decode split-K vs single pass, 128K non-causal,
       512 x 128K fused vs separate): median and min of timed runs per call.
+  python bench.py --sweep crossover|splitk|context
+      the ablations: fused vs separate backward over N_Q at N_K = 128K; split-K
+      vs one pass (and several split counts) over small N_Q; and latency,
+      TFLOP/s and device memory over context length 4K..512K.  One JSON line
+      per point.
   python bench.py --copy-calibration ...
       also runs one plain 1 GiB device copy first, so that a rocprofv3 --pmc
       run sees FETCH_SIZE / WRITE_SIZE of a copy of known size.
@@ -231,6 +236,113 @@ def configs_mode():
     run("smallq128k", (2,), paths=("auto", "fused", "separate"))
 
 
+def _rand_inputs(heads, n_q, n_k, d, seed=0, corr=True):
+    """Sweep inputs drawn on the device (timing only; parity is covered by the tests)."""
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    q1 = torch.randn(heads, n_q, d, device="cuda", generator=g, dtype=torch.bfloat16)
+    k1 = torch.randn(heads, n_k, d, device="cuda", generator=g, dtype=torch.bfloat16)
+    q2 = torch.randn(heads, n_q, d, device="cuda", generator=g, dtype=torch.bfloat16)
+    k2 = torch.randn(heads, n_k, d, device="cuda", generator=g, dtype=torch.bfloat16)
+    if corr:
+        q2 = (q1.float() + 0.3 * q2.float()).to(torch.bfloat16)
+        k2 = (k1.float() + 0.3 * k2.float()).to(torch.bfloat16)
+    return q1, k1, q2, k2
+
+
+def sweep_mode(which: str):
+    import torch
+    import streaming_kl_divergence_amd as skl
+    stream = torch.cuda.current_stream()
+    H, d = 32, 128
+    scale = d ** -0.5
+
+    def emit(**kw):
+        print(json.dumps({"sweep": which, **kw}), flush=True)
+
+    def pairs(n_q, n_k, causal):
+        if not causal:
+            return H * n_q * n_k
+        off = n_k - n_q
+        return H * sum(min(n_k, i + off + 1) for i in range(n_q)) if n_q < 4096 else \
+            H * (n_q * (n_q + 1) // 2 + n_q * off)
+
+    if which == "crossover":
+        # fused (one recompute, fp32 atomics into dQ) vs separate (dK and dQ
+        # kernels, two recomputes), N_K = 128K, non-causal, both settings
+        n_k = 131072
+        for n_q in (64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384):
+            q1, k1, q2, k2 = _rand_inputs(H, n_q, n_k, d)
+            kl, l1, l2 = skl.fwd(q1, k1, q2, k2, scale, False)
+            dq = torch.empty(H, n_q, d, device="cuda")
+            dk = torch.empty(H, n_k, d, device="cuda")
+            E = H * n_q * n_k
+            row = {"n_q": n_q, "n_k": n_k, "heads": H, "dq_mib": H * n_q * d * 4 / 2 ** 20,
+                   "selector": skl.bwd_select(n_q, n_k, H, d, False)}
+            for st in (1, 2):
+                kw = dict(kl=kl) if st == 2 else {}
+                for path in ("fused", "separate"):
+                    ms = np.median(_timed(lambda: skl.bwd(st, q1, k1, q2, k2, scale, False, l1, l2, path=path,
+                                                          dq=dq, dk=dk, **kw), stream, 2, 5))
+                    row[f"set{st}_{path}_ms"] = round(float(ms), 4)
+                    row[f"set{st}_{path}_tflops"] = round(8 * d * E / (ms * 1e-3) / 1e12, 1)
+                row[f"set{st}_fused_over_separate"] = round(row[f"set{st}_separate_ms"] / row[f"set{st}_fused_ms"], 3)
+            emit(**row)
+            del q1, k1, q2, k2, dq, dk
+            torch.cuda.empty_cache()
+    elif which == "splitk":
+        # forward with few queries: one pass vs split-K (automatic and fixed counts)
+        n_k = 524288
+        q1, k1, q2, k2 = _rand_inputs(H, 256, n_k, d, corr=False)
+        for n_q in (1, 4, 16, 64, 256):
+            a = [t[:, :n_q].contiguous() if i % 2 == 0 else t for i, t in enumerate((q1, k1, q2, k2))]
+            hbm = 2 * H * n_k * d * 2
+            auto = skl.splitk_auto(n_q, n_k, H, d)
+            row = {"n_q": n_q, "n_k": n_k, "heads": H, "auto_splits": auto}
+            ms = np.median(_timed(lambda: skl.fwd(*a, scale, False), stream, 2, 5))
+            row["one_pass_ms"] = round(float(ms), 4)
+            for sp in sorted({1, 8, 32, 64, 128, 256, auto}):
+                ms = np.median(_timed(lambda: skl.fwd_splitk(*a, scale, False, num_splits=sp), stream, 2, 5))
+                row[f"splits_{sp}_ms"] = round(float(ms), 4)
+            row["auto_gbs"] = round(hbm / (row[f"splits_{auto}_ms"] * 1e-3) / 1e9, 1)
+            row["speedup_auto_over_one_pass"] = round(row["one_pass_ms"] / row[f"splits_{auto}_ms"], 2)
+            emit(**row)
+    elif which == "context":
+        # latency, algorithmic TFLOP/s and the library's extra device memory
+        # (saved state only: KL, LSE1, LSE2) over context length
+        for causal in (True, False):
+            for n in (4096, 16384, 65536, 131072, 262144, 524288):
+                if not causal and n > 262144:
+                    continue
+                q1, k1, q2, k2 = _rand_inputs(H, n, n, d)
+                E = pairs(n, n, causal)
+                torch.cuda.synchronize()
+                base = torch.cuda.memory_allocated()
+                torch.cuda.reset_peak_memory_stats()
+                kl, l1, l2 = skl.fwd(q1, k1, q2, k2, scale, causal)
+                torch.cuda.synchronize()
+                state = torch.cuda.max_memory_allocated() - base
+                reps = 3 if n <= 65536 else 1
+                row = {"n": n, "causal": causal, "heads": H, "pairs": E, "saved_state_bytes": int(state),
+                       "materialised_p_bytes": 2 * E * 2}
+                ms = np.median(_timed(lambda: skl.fwd(q1, k1, q2, k2, scale, causal), stream, 1, reps))
+                row["fwd_ms"] = round(float(ms), 3)
+                row["fwd_tflops"] = round(4 * d * E / (ms * 1e-3) / 1e12, 1)
+                dq = torch.empty(H, n, d, device="cuda")
+                dk = torch.empty(H, n, d, device="cuda")
+                for st in (1, 2):
+                    kw = dict(kl=kl) if st == 2 else {}
+                    ms = np.median(_timed(lambda: skl.bwd(st, q1, k1, q2, k2, scale, causal, l1, l2, dq=dq, dk=dk,
+                                                          **kw), stream, 1, reps))
+                    row[f"bwd_set{st}_ms"] = round(float(ms), 3)
+                    row[f"bwd_set{st}_tflops"] = round(8 * d * E / (ms * 1e-3) / 1e12, 1)
+                emit(**row)
+                del q1, k1, q2, k2, dq, dk, kl, l1, l2
+                torch.cuda.empty_cache()
+    else:
+        raise SystemExit(f"unknown sweep {which!r}")
+
+
 def cpu_baseline():
     """The fp64 oracle, as it stands, on a bounded sample of the same workload:
     head 0 of the 64K causal workload restricted to its first 16384 queries and
@@ -265,6 +377,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", default="causal64k")
     ap.add_argument("--configs", action="store_true")
+    ap.add_argument("--sweep", choices=("crossover", "splitk", "context"))
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     args = ap.parse_args()
@@ -288,6 +401,9 @@ def main():
         del src, dst
     if args.configs:
         configs_mode()
+        return
+    if args.sweep:
+        sweep_mode(args.sweep)
         return
     w = W.WORKLOADS[args.workload]
     threads = min(16, os.cpu_count() or 1)

@@ -151,7 +151,10 @@ size_t streamkl_workspace_bytes(int op, int n_q, int n_k, int heads, int head_di
 int streamkl_splitk_auto(int n_q, int n_k, int heads, int head_dim);
 
 /* The backward path AUTO resolves to for this shape (STREAMKL_BWD_FUSED or
- * STREAMKL_BWD_SEPARATE). */
+ * STREAMKL_BWD_SEPARATE).  The pages (Methodology 3, Kernel Fusion) prefer the
+ * fused kernel while the dQ buffer fits the cache; on MI355X its fp32 atomics
+ * made it slower than the separate kernels at every measured size, so this
+ * returns STREAMKL_BWD_SEPARATE for every shape. */
 int streamkl_bwd_select(int n_q, int n_k, int heads, int head_dim, int causal);
 
 /* Static text for a status code. */

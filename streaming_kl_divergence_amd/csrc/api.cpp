@@ -148,13 +148,19 @@ int streamkl_fwd_splitk(const void* q1, const void* k1, const void* q2, const vo
 }
 
 int streamkl_bwd_select(int n_q, int n_k, int heads, int head_dim, int causal) {
+  (void)n_q;
   (void)n_k;
+  (void)heads;
+  (void)head_dim;
   (void)causal;
-  // The fused kernel adds every workgroup's dQ tile into dQ with fp32
-  // atomics.  It wins only while that buffer is small enough to stay in the
-  // on-chip caches; otherwise the separate dK and dQ kernels are used.
-  const double dq_bytes = (double)heads * n_q * head_dim * 4.0;
-  return dq_bytes <= 16.0 * 1024 * 1024 ? STREAMKL_BWD_FUSED : STREAMKL_BWD_SEPARATE;
+  // The pages' rule (Methodology 3, Kernel Fusion) takes the fused kernel while
+  // dQ fits the cache.  On MI355X the fused kernel moves 4*d/128 bytes of fp32
+  // atomics per (query, key) pair, about six times the time of the score
+  // recomputation it saves, and measured slower than the separate kernels at
+  // every size tried: 0.94x at 64 queries x 128K keys (dQ 1 MiB) down to
+  // 0.44x at 16K queries, both settings.  So AUTO takes the separate kernels;
+  // the fused path stays available on request.
+  return STREAMKL_BWD_SEPARATE;
 }
 
 // Key ranges for the separate path's dQ kernel: enough workgroups to fill the
