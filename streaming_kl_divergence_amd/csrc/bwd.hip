@@ -225,8 +225,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int h = lane >> 5;
   const int col = lane & 31;
 
-  const int head = blockIdx.x % p.heads;
-  const int kb = blockIdx.x / p.heads;
+  const int nkb = (p.n_k + C::BKW - 1) / C::BKW;
+  const int w = xcd_work_index(blockIdx.x, p.heads * nkb);
+  if (w >= p.heads * nkb) return;
+  const int head = w / nkb;
+  const int kb = w % nkb;   // key block 0 (heaviest when causal) first
   const int k0 = kb * C::BKW;
   const int kw0 = k0 + wave * 32;
   const int key = kw0 + col;
@@ -480,12 +483,17 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdParams p) {
 
   const int nqb = (p.n_q + BQ - 1) / BQ;
   int bid = blockIdx.x;
-  const int head = bid % p.heads;
-  bid /= p.heads;
-  int split = 0;
+  int head, split = 0;
   if (SPLIT) {
+    head = bid % p.heads;
+    bid /= p.heads;
     split = bid % p.dq_splits;
     bid /= p.dq_splits;
+  } else {
+    const int w = xcd_work_index(bid, p.heads * nqb);
+    if (w >= p.heads * nqb) return;
+    head = w / nqb;
+    bid = w % nqb;
   }
   const int qb = p.causal ? (nqb - 1 - bid) : bid;
   const int off = p.n_k - p.n_q;
@@ -644,7 +652,8 @@ static hipError_t sep(const BwdParams& p, bool do_dk, bool do_dq, hipStream_t s)
   hipError_t e = hipSuccess;
   if (do_dk) {
     const int nkb = (p.n_k + KC::BKW - 1) / KC::BKW;
-    hipLaunchKernelGGL((bwd_kv_kernel<T, D, SETTING, false, HAS_G>), dim3(p.heads * nkb), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_kv_kernel<T, D, SETTING, false, HAS_G>), dim3(xcd_grid(p.heads * nkb)), dim3(256), 0, s,
+                       p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -656,7 +665,7 @@ static hipError_t sep(const BwdParams& p, bool do_dk, bool do_dq, hipStream_t s)
     hipLaunchKernelGGL((bwd_q_kernel<T, D, SETTING, true, HAS_G>), dim3(p.heads * nqb * p.dq_splits), dim3(256), 0, s,
                        p);
   } else {
-    hipLaunchKernelGGL((bwd_q_kernel<T, D, SETTING, false, HAS_G>), dim3(p.heads * nqb), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((bwd_q_kernel<T, D, SETTING, false, HAS_G>), dim3(xcd_grid(p.heads * nqb)), dim3(256), 0, s, p);
   }
   return hipGetLastError();
 }
@@ -667,7 +676,7 @@ static hipError_t fused(const BwdParams& p, hipStream_t s) {
   hipError_t e = zero_fill(p.dq, (size_t)p.heads * p.n_q * D, s);
   if (e != hipSuccess) return e;
   const int nkb = (p.n_k + KC::BKW - 1) / KC::BKW;
-  hipLaunchKernelGGL((bwd_kv_kernel<T, D, SETTING, true, HAS_G>), dim3(p.heads * nkb), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((bwd_kv_kernel<T, D, SETTING, true, HAS_G>), dim3(xcd_grid(p.heads * nkb)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -86,6 +86,20 @@ __device__ __forceinline__ f32x16 mfma_chunk<float>(u32x4 a, u32x4 b, f32x16 acc
   return acc;
 }
 
+// Launch order -> work order.  The hardware deals workgroups round-robin over
+// the XCDs (launch index i runs on XCD i mod 8).  Work items (head, block)
+// are numbered head-major, and XCD x takes the contiguous range
+// [x * per, (x + 1) * per) of them in order, so the workgroups resident on an
+// XCD at any time belong to one head and stream the same key (or query) tiles
+// through that XCD's L2.  The grid has kXcds * per workgroups; a returned
+// index >= total marks a workgroup with nothing to do.
+constexpr int kXcds = 8;
+__host__ __device__ inline int xcd_grid(int total) { return kXcds * ((total + kXcds - 1) / kXcds); }
+__device__ __forceinline__ int xcd_work_index(int bid, int total) {
+  const int per = (total + kXcds - 1) / kXcds;
+  return (bid % kXcds) * per + bid / kXcds;
+}
+
 // Row index (within a 32 x 32 MFMA result block) of register r in lane half h.
 __device__ __forceinline__ int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 

@@ -27,9 +27,9 @@
 //   * Causal: Q blocks are launched heaviest first; tiles past a wave's
 //     frontier are skipped; only tiles that cross the diagonal or the end of
 //     the key range take the masked code path.
-//   * Workgroup ids map head-fastest, so all blocks of one head go to the
-//     same XCD (blocks are dealt round-robin over the 8 XCDs) and share its
-//     L2 for the K stream.
+//   * Each XCD walks a contiguous run of (head, query block) items, one head
+//     at a time (xcd_work_index), so the workgroups resident on an XCD stream
+//     the same K tiles through its L2.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -184,14 +184,19 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
 
   const int nqb = (p.n_q + BQ - 1) / BQ;
   int bid = blockIdx.x;
-  const int head = bid % p.heads;
-  bid /= p.heads;
-  int split = 0;
+  int head, split = 0;
   if (SPLIT) {
+    head = bid % p.heads;
+    bid /= p.heads;
     split = bid % p.splits;
     bid /= p.splits;
+  } else {
+    const int w = xcd_work_index(bid, p.heads * nqb);
+    if (w >= p.heads * nqb) return;
+    head = w / nqb;
+    bid = w % nqb;
   }
-  const int qb = p.causal ? (nqb - 1 - bid) : bid;
+  const int qb = p.causal ? (nqb - 1 - bid) : bid;   // causal: heaviest blocks first
 
   const int off = p.n_k - p.n_q;
   const int q0 = qb * BQ;
@@ -327,7 +332,7 @@ __global__ __launch_bounds__(256) void splitk_combine_kernel(FwdParams p) {
 template <typename T, int D, int NW, bool SPLIT>
 static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
   const int nqb = (p.n_q + 32 * NW - 1) / (32 * NW);
-  const long long blocks = (long long)p.heads * nqb * (SPLIT ? p.splits : 1);
+  const long long blocks = SPLIT ? (long long)p.heads * nqb * p.splits : (long long)xcd_grid(p.heads * nqb);
   hipLaunchKernelGGL((fwd_kernel<T, D, NW, SPLIT>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
