@@ -207,8 +207,11 @@ struct KvCfg {
   static constexpr int kLdsFused = kLdsBase + KT::kBytes + DS::kBytes;
 };
 
+// bf16 separate path: two waves per SIMD (256 VGPRs); the fp32 and fused
+// instantiations need more registers and run one wave per SIMD.
 template <typename T, int D, int SETTING, bool FUSED, bool HAS_G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_kv_kernel(BwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((sizeof(T) == 2 && !FUSED) ? 2 : 1)))
+void bwd_kv_kernel(BwdParams p) {
   using G = Geom<T, D>;
   using C = KvCfg<T, D>;
   constexpr int NW = C::NW, BT = C::BT, NQB = C::NQB, TILE = C::TILE, DB = D / 32;
