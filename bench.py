@@ -74,7 +74,8 @@ def upload(w: W.Workload, threads: int):
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in sorted(os.listdir(os.path.join(ROOT, "streaming_kl_divergence_amd", "csrc"))):
-        h.update(open(os.path.join(ROOT, "streaming_kl_divergence_amd", "csrc", f), "rb").read())
+        with open(os.path.join(ROOT, "streaming_kl_divergence_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -84,7 +85,8 @@ def measured_traffic(kernel: str):
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
-    d = json.load(open(p))
+    with open(p) as f:
+        d = json.load(f)
     e = d.get(kernel)
     if not e or e.get("source_hash") != kernel_source_hash():
         return None
@@ -151,7 +153,8 @@ def pmc_summary(fetch_dir: str, write_dir: str):
         table[label] = {"symbol": name, "dispatches": len(v), "fetch_bytes": round(fb), "write_bytes": round(wb),
                         "bytes_per_launch": round(fb + wb), "source_hash": h}
     path = os.path.join(ROOT, "profiles", "traffic.json")
-    json.dump(table, open(path, "w"), indent=1, sort_keys=True)
+    with open(path, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
     print(json.dumps(table, indent=1, sort_keys=True))
 
 

@@ -15,7 +15,8 @@ FAKE = 4096  # a non-NULL, 16-byte aligned address that is never dereferenced
 
 
 def declared_functions():
-    src = open(HEADER).read()
+    with open(HEADER) as f:
+        src = f.read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(streamkl_\w+)\s*\(", src)))
 

@@ -19,7 +19,8 @@ def test_pin(pin):
 
 
 def _mutant(old: str, new: str) -> types.ModuleType:
-    src = open(ORACLE_SRC).read()
+    with open(ORACLE_SRC) as f:
+        src = f.read()
     assert src.count(old) >= 1, old
     mod = types.ModuleType("oracle_mutant")
     exec(compile(src.replace(old, new), "oracle_mutant", "exec"), mod.__dict__)
@@ -75,7 +76,8 @@ def test_page_memory_figure():
     32 heads, BF16 takes about 512 GB (StreamKL gist.science technical summary,
     Problem Statement)."""
     import json
-    golden = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")))
+    with open(os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")) as f:
+        golden = json.load(f)
     f = golden["materialized_p1_p2_bytes"]
     n, heads, bytes_per = f["context"], f["heads"], f["bytes_per_element"]
     total = 2 * n * n * heads * bytes_per
