@@ -55,6 +55,7 @@ BWD_EDGE = [
     (2, 70, 1, 128, "bf16", False, 1.0),
     (2, 400, 900, 128, "bf16", True, 4.0),
     (1, 128, 128, 128, "bf16", True, 1.0),
+    (2, 200, 300, 128, "bf16", True, 0.0),    # scale 0: uniform rows, zero gradients
 ]
 
 
@@ -150,3 +151,25 @@ def test_smallq128k_setting2_paths():
         for path, (dq, dk) in res.items():
             compare(dq[h], rdq, "bf16", f"{path} h{h} dq1")
             compare(dk[h, keys], rdk, "bf16", f"{path} h{h} dk1")
+
+
+@pytest.mark.parametrize("path", ["separate", "fused"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_teacher_and_student_give_exact_zeros(causal, path):
+    """(Q1, K1) = (Q2, K2): both distributions go through the same arithmetic,
+    so KL and every gradient of both settings are exactly zero (bitwise)."""
+    need_gpu()
+    import torch
+    import streaming_kl_divergence_amd as skl
+    log(f"case identical inputs causal={causal} path={path}")
+    rng = np.random.default_rng(77)
+    q = W.round_bf16(rng.standard_normal((2, 300, 128), dtype=np.float32))
+    k = W.round_bf16(rng.standard_normal((2, 500, 128), dtype=np.float32))
+    q1, k1, q2, k2 = device_inputs([q, k, q, k], "bf16")
+    kl, l1, l2 = skl.fwd(q1, k1, q2, k2, 0.09, causal)
+    assert torch.equal(kl, torch.zeros_like(kl)) and torch.equal(l1, l2)
+    for setting in (1, 2):
+        kw = dict(kl=kl) if setting == 2 else {}
+        dq, dk = skl.bwd(setting, q1, k1, q2, k2, 0.09, causal, l1, l2, path=path, **kw)
+        torch.cuda.synchronize()
+        assert not bool(dq.any()) and not bool(dk.any()), f"setting {setting}: nonzero gradient"
