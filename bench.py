@@ -123,11 +123,12 @@ def pmc_summary(fetch_dir: str, write_dir: str):
         if not f:
             raise SystemExit(f"no counter_collection.csv under {d}")
         vals = {}
-        for r in csv.DictReader(open(f[0])):
-            if r["Counter_Name"] != counter:
-                continue
-            key = (r["Kernel_Name"], r.get("Dispatch_Id", r.get("Correlation_Id", "")))
-            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"]) * 1024.0
+        with open(f[0]) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Kernel_Name"], r.get("Dispatch_Id", r.get("Correlation_Id", "")))
+                vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"]) * 1024.0
         out = {}
         for (name, _), v in vals.items():
             out.setdefault(name, []).append(v)

@@ -123,17 +123,18 @@ __device__ __forceinline__ f32x16 kgroup_mfma<float>(const SKL_LDS char* xrow, i
 }
 
 // bf16 form of kgroup_mfma: the A operand (X^T rows = 32 columns of the
-// row-major LDS tile starting at element column c0; k = tile rows rbase ..
-// rbase+31) comes straight from the row-major tile through transposing reads.
+// row-major LDS tile starting at element column 32 db; k = tile rows rbase ..
+// rbase+31) comes straight from the row-major tile through transposing reads
+// (tb: the lane's tr_base for hi = 0 and 1).
 template <int D>
-__device__ __forceinline__ f32x16 kgroup_mfma_tr(const SKL_LDS char* tile, int rbase, int c0, int lane,
+__device__ __forceinline__ f32x16 kgroup_mfma_tr(const SKL_LDS char* tile, int rbase, int db, const int* tb,
                                                  const float* v, f32x16 acc) {
-  const int h = lane >> 5;
-  const int cl = c0 + 16 * ((lane >> 4) & 1);
+  constexpr int RB = D * 2;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const u32x2 lo = read_tr4<D>(tile, rbase + 16 * t + 4 * h, cl, lane);
-    const u32x2 hi = read_tr4<D>(tile, rbase + 16 * t + 8 + 4 * h, cl, lane);
+    const SKL_LDS char* rows = tile + (rbase + 16 * t) * RB;
+    const u32x2 lo = read_tr4_at(rows + (tb[0] ^ (64 * db)));
+    const u32x2 hi = read_tr4_at(rows + (tb[1] ^ (64 * db)));
     const u32x4 a = u32x4{lo.x, lo.y, hi.x, hi.y};
     bf16x8 b;
 #pragma unroll
@@ -238,6 +239,8 @@ void bwd_kv_kernel(BwdParams p) {
   const int key = kw0 + col;
   const int off = p.n_k - p.n_q;
   const float c = p.c;
+  const int pb = pair_base<T, D>(col, h);                              // operand reads of S
+  const int tb[2] = {tr_base<D>(lane, 0), tr_base<D>(lane, 1)};        // transposing reads
 
   const size_t hq = (size_t)head * p.n_q;
   const size_t hk = (size_t)head * p.n_k;
@@ -353,7 +356,7 @@ void bwd_kv_kernel(BwdParams p) {
         __builtin_amdgcn_s_setprio(1);   // MFMA phase first when two waves share a SIMD
 #pragma unroll
         for (int g = 0; g < G::kGroups; ++g) {
-          const int ob = lds_chunk_off<T, D>(qb * 32 + col, 2 * g + h);
+          const int ob = pair_off(pb, g) + qb * 32 * G::kRowBytes;
           s1 = mfma_chunk<T>(*(const SKL_LDS u32x4*)(t1 + ob), kf1[g], s1);
           s2 = mfma_chunk<T>(*(const SKL_LDS u32x4*)(t2 + ob), kf2[g], s2);
         }
@@ -389,7 +392,7 @@ void bwd_kv_kernel(BwdParams p) {
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           if constexpr (C::TR)
-            dkt[db] = kgroup_mfma_tr<D>(tsrc, qb * 32, db * 32, lane, ds, dkt[db]);
+            dkt[db] = kgroup_mfma_tr<D>(tsrc, qb * 32, db, tb, ds, dkt[db]);
           else
             dkt[db] = kgroup_mfma<T>(qt + (db * 32 + col) * C::QT::kStride, qb * 32, h, ds, dkt[db]);
         }
@@ -504,6 +507,8 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdParams p) {
   const int qw0 = q0 + wave * 32;
   const int qrow = qw0 + col;
   const float c = p.c;
+  const int pb = pair_base<T, D>(col, h);                              // operand reads of S
+  const int tb[2] = {tr_base<D>(lane, 0), tr_base<D>(lane, 1)};        // transposing reads
 
   int kbeg = 0, klimit = p.n_k;
   if (SPLIT) {
@@ -583,7 +588,7 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdParams p) {
       __builtin_amdgcn_s_setprio(1);   // MFMA phase first when two waves share a SIMD
 #pragma unroll
       for (int g = 0; g < G::kGroups; ++g) {
-        const int ob = lds_chunk_off<T, D>(kb * 32 + col, 2 * g + h);
+        const int ob = pair_off(pb, g) + kb * 32 * G::kRowBytes;
         s1 = mfma_chunk<T>(*(const SKL_LDS u32x4*)(t1 + ob), qf1[g], s1);
         s2 = mfma_chunk<T>(*(const SKL_LDS u32x4*)(t2 + ob), qf2[g], s2);
       }
@@ -604,7 +609,7 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdParams p) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         if constexpr (C::TR)
-          dqt[db] = kgroup_mfma_tr<D>(tsrc, kb * 32, db * 32, lane, ds, dqt[db]);
+          dqt[db] = kgroup_mfma_tr<D>(tsrc, kb * 32, db, tb, ds, dqt[db]);
         else
           dqt[db] = kgroup_mfma<T>(kt + (db * 32 + col) * C::KT::kStride, kb * 32, h, ds, dqt[db]);
       }

@@ -57,6 +57,18 @@ __device__ __forceinline__ int lds_chunk_off(int row, int c) {
   return (row * G::kChunks + (c ^ row_swizzle<G::kChunks>(row))) * 16;
 }
 
+// Offsets of the MFMA operand reads in closed form.  The swizzle depends only
+// on row mod 16 and XORs the chunk index, and row bits and chunk bits of an
+// offset never overlap, so for r0 a multiple of 16
+//   lds_chunk_off(r0 + col, 2 g + h) = (pair_base ^ 32 g) + r0 * row_bytes,
+//   pair_base = lds_chunk_off(col, h).
+// One per-lane base serves every row block and chunk pair: each read costs
+// one XOR-add, and the row block and the tile's place in LDS become the
+// instruction's immediate offset.
+template <typename T, int D>
+__device__ __forceinline__ int pair_base(int col, int h) { return lds_chunk_off<T, D>(col, h); }
+__device__ __forceinline__ int pair_off(int base, int g) { return base ^ (32 * g); }
+
 // acc(32 x 32) += A(32 x k) B(k x 32) for one chunk pair.  Lane l supplies one
 // 16-byte chunk of row (l % 32) of A and of column (l % 32) of B; lanes l and
 // l + 32 hold the two chunks of the pair.  Any fixed assignment of a row's
@@ -250,14 +262,25 @@ __device__ __forceinline__ void wait_async_loads() { __builtin_amdgcn_s_waitcnt(
 // ds_read_b64_tr_b16 on gfx950: result[i][e] = loaded[4e + i/4][i % 4]
 // within each group of 16 lanes.)
 template <int D>
-__device__ __forceinline__ u32x2 read_tr4(const SKL_LDS char* tile, int r0, int c0, int lane) {
+__device__ __forceinline__ int tr4_off(int r0, int c0, int lane) {
   const int l16 = lane & 15;
   const int row = r0 + (l16 >> 2);
   const int cc = c0 + 4 * (l16 & 3);            // bf16 element column
-  const int off = lds_chunk_off<__bf16, D>(row, cc >> 3) + (cc & 7) * 2;
+  return lds_chunk_off<__bf16, D>(row, cc >> 3) + (cc & 7) * 2;
+}
+__device__ __forceinline__ u32x2 read_tr4_at(const SKL_LDS char* p) {
   typedef short s16x4 __attribute__((ext_vector_type(4)));
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SKL_LDS s16x4*)(tile + off));
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SKL_LDS s16x4*)p);
   return __builtin_bit_cast(u32x2, v);
+}
+
+// The transposing reads of one 32 x 32 block in closed form, as for pair_base:
+// lane l reads rows rb + 16 t + 4 (l / 32) + 8 hi + (l % 16) / 4 (t, hi = 0, 1)
+// at element column 32 db + 16 ((l / 16) % 2) + 4 (l % 4); for rb a multiple
+// of 32 the offset is (tr_base(hi) ^ 64 db) + (rb + 16 t) * row_bytes.
+template <int D>
+__device__ __forceinline__ int tr_base(int lane, int hi) {
+  return tr4_off<D>(4 * (lane >> 5) + 8 * hi, 16 * ((lane >> 4) & 1), lane);
 }
 
 }  // namespace skl

@@ -41,9 +41,10 @@ struct RowState {
 };
 
 // S1, S2 (raw units) of one 64-key tile for this lane's query: 2 blocks of 16.
+// pb: the lane's pair_base.
 template <typename T, int D, int NKB>
 __device__ __forceinline__ void tile_scores(const SKL_LDS char* t1, const SKL_LDS char* t2, const u32x4* qf1,
-                                            const u32x4* qf2, int col, int h, f32x16* s1, f32x16* s2) {
+                                            const u32x4* qf2, int pb, f32x16* s1, f32x16* s2) {
   using G = Geom<T, D>;
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
@@ -51,7 +52,7 @@ __device__ __forceinline__ void tile_scores(const SKL_LDS char* t1, const SKL_LD
     s2[kb] = f32x16{};
 #pragma unroll
     for (int g = 0; g < G::kGroups; ++g) {
-      const int ob = lds_chunk_off<T, D>(kb * 32 + col, 2 * g + h);
+      const int ob = pair_off(pb, g) + kb * 32 * G::kRowBytes;
       s1[kb] = mfma_chunk<T>(*(const SKL_LDS u32x4*)(t1 + ob), qf1[g], s1[kb]);
       s2[kb] = mfma_chunk<T>(*(const SKL_LDS u32x4*)(t2 + ob), qf2[g], s2[kb]);
     }
@@ -241,6 +242,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   RowState st{kMaxInit, kMaxInit, 0.f, 0.f, 0.f};
   const float c = p.c;
   const int qlim = qrow + off;   // last key this lane's query may see (causal)
+  const int pb = pair_base<T, D>(col, h);
 
   // Two waves per SIMD (223 VGPRs) overlap one wave's MFMAs with the other's VALU.
   f32x16 s1[NKB], s2[NKB];
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
     const bool need_mask = (k0 + BK > klimit) || (p.causal && k0 + BK - 1 > qw0 + off);
     const SKL_LDS char* cur = lds + buf * 2 * TILE;
     __builtin_amdgcn_s_setprio(1);   // MFMA phase first when two waves share a SIMD
-    tile_scores<T, D, NKB>(cur, cur + TILE, qf1, qf2, col, h, s1, s2);
+    tile_scores<T, D, NKB>(cur, cur + TILE, qf1, qf2, pb, s1, s2);
     __builtin_amdgcn_s_setprio(0);
     if (need_mask) {
       tile_update<true, NKB>(st, s1, s2, c, k0, h, klimit, p.causal, qlim);
