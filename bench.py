@@ -31,6 +31,10 @@ Usage:
       --copy-calibration run), scales each counter by what it reads for the
       1 GiB copy, and writes profiles/traffic.json (HBM bytes per launch per
       kernel, tagged with a hash of the kernel sources).
+  python bench.py --sq-summary DIR [DIR ...]
+      reads rocprofv3 --pmc outputs holding SQ counters and GRBM_GUI_ACTIVE
+      and prints, per kernel, how busy the matrix cores, the vector ALU and
+      the LDS were and the shader clock the kernel ran at (markdown table).
 """
 from __future__ import annotations
 
@@ -157,6 +161,55 @@ def pmc_summary(fetch_dir: str, write_dir: str):
     with open(path, "w") as f:
         json.dump(table, f, indent=1, sort_keys=True)
     print(json.dumps(table, indent=1, sort_keys=True))
+
+
+SIMDS, CUS, XCDS = 1024, 256, 8
+
+
+def sq_summary(dirs):
+    """Pipe utilisation per kernel from SQ counters (one or more --pmc runs of
+    the same program; the last dispatch of each kernel is used).  Cycles are
+    shader-clock cycles: GRBM_GUI_ACTIVE summed over the XCDs, divided by
+    their number, is the kernel's length in cycles; the clock is that over
+    the dispatch's duration."""
+    import csv
+    import glob
+    per = {}
+    for d in dirs:
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not f:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        disp = {}
+        with open(f[0]) as fh:
+            for r in csv.DictReader(fh):
+                label = kernel_label(r["Kernel_Name"])
+                if label is None:
+                    continue
+                e = disp.setdefault(int(r["Dispatch_Id"]), {"label": label, "c": {}})
+                e["c"][r["Counter_Name"]] = e["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                e["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        for i in sorted(disp):
+            e = disp[i]
+            dst = per.setdefault(e["label"], {"c": {}, "ns": {}})
+            dst["c"].update(e["c"])
+            dst["ns"][d] = e["ns"]
+    rows = ["| kernel | clock GHz | MFMA busy | VALU busy | MFMA+VALU co-issue | LDS busy | VALU instr / MFMA |",
+            "|---|---|---|---|---|---|---|"]
+    for label, e in per.items():
+        c = e["c"]
+        if "GRBM_GUI_ACTIVE" not in c:
+            continue
+        cyc = c["GRBM_GUI_ACTIVE"] / XCDS
+
+        def frac(name, scale=1.0, units=SIMDS):
+            return f"{100 * c[name] * scale / units / cyc:.0f}%" if name in c else "-"
+
+        ghz = cyc / (float(np.mean(list(e["ns"].values()))))
+        ratio = f"{c['SQ_INSTS_VALU'] / c['SQ_INSTS_MFMA']:.2f}" if "SQ_INSTS_VALU" in c and c.get("SQ_INSTS_MFMA") else "-"
+        rows.append(f"| {label} | {ghz:.2f} | {frac('SQ_VALU_MFMA_BUSY_CYCLES')} | "
+                    f"{frac('SQ_ACTIVE_INST_VALU', 4.0)} | {frac('SQ_VALU_MFMA_COEXEC_CYCLES')} | "
+                    f"{frac('SQ_LDS_IDX_ACTIVE', 1.0, CUS)} | {ratio} |")
+    print("\n".join(rows))
 
 
 def _timed(fn, stream, warmup: int, reps: int):
@@ -384,9 +437,13 @@ def main():
     ap.add_argument("--sweep", choices=("crossover", "splitk", "context"))
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--sq-summary", nargs="+", metavar="DIR")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
+        return
+    if args.sq_summary:
+        sq_summary(args.sq_summary)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
