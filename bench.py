@@ -4,12 +4,16 @@ One step = the whole path on one batch of the 64K causal workload (32 heads,
 N_Q = N_K = 65536, head_dim 128, bf16, student near teacher, seed 2):
 forward (KL, LSE1, LSE2) + backward Setting 1 (dQ2, dK2) + backward Setting 2
 (dQ1, dK1), each through the C ABI on the current stream, inputs resident in
-HBM before the timed region starts.
+HBM before the timed region starts.  The two settings' gradients come from
+one recomputation (streamkl_bwd_both: its dK kernel, then its dQ kernel);
+--bwd-path separate times the two single-setting passes instead.
 
 value = algorithmic TFLOP per step / seconds per step, where the algorithmic
 work counts only unmasked (query, key) pairs: 4 d flop each in the forward and
-8 d in each backward setting (recomputation once; the separate path's second
-recomputation is not counted).
+8 d in each backward setting (the scores recomputed once, 4 d, and the dQ and
+dK products, 4 d).  The both-settings kernels execute exactly this work (8 d
+per pair each); the single-setting path executes 12 d per setting, its second
+recomputation not counted.
 
 Usage:
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -100,11 +104,12 @@ def measured_traffic(kernel: str):
 def kernel_label(symbol: str):
     """Benchmark label of a library kernel symbol (None for other kernels)."""
     import re
-    m = re.match(r"_ZN3skl(\d+)(fwd_kernel|bwd_kv_kernel|bwd_q_kernel|splitk_combine_kernel)(.*)$", symbol)
+    m = re.match(r"_ZN3skl(\d+)(fwd_kernel|bwd_kv_kernel|bwd_q_kernel|bwd_kv_both_kernel|bwd_q_both_kernel|"
+                 r"splitk_combine_kernel)(.*)$", symbol)
     if not m:
         return None
     name, targs = m.group(2), m.group(3)
-    if name in ("fwd_kernel", "splitk_combine_kernel"):
+    if name in ("fwd_kernel", "splitk_combine_kernel", "bwd_kv_both_kernel", "bwd_q_both_kernel"):
         return name
     st = re.search(r"Li\d+ELi(\d)ELb(\d)", targs)
     setting, flag = (st.group(1), st.group(2)) if st else ("?", "0")
@@ -438,6 +443,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--sq-summary", nargs="+", metavar="DIR")
+    ap.add_argument("--bwd-path", choices=("both", "separate"), default="both",
+                    help="backward of the step: both settings from one recomputation (default), or the two "
+                         "single-setting passes with the library's path choice")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
@@ -478,15 +486,20 @@ def main():
     flop_bwd = 8 * d * E
     flop_step = flop_fwd + 2 * flop_bwd
     stream = torch.cuda.current_stream()
-    path = skl.bwd_select(w.n_q, w.n_k, w.heads, d, causal)
+    # the step needs both settings' gradients: by default one recomputation
+    # serves both (streamkl_bwd_both); --bwd-path separate times the two
+    # single-setting backward passes instead
+    path = args.bwd_path if args.bwd_path == "both" else skl.bwd_select(w.n_q, w.n_k, w.heads, d, causal)
     # every call below launches one kernel, so the events around it time that kernel
-    if path == "separate":
+    if path == "both":
+        calls = [("fwd_kernel", 4), ("bwd_kv_both_kernel", 8), ("bwd_q_both_kernel", 8)]
+    elif path == "separate":
         calls = [("fwd_kernel", 4), ("bwd_kv_kernel set1", 6), ("bwd_q_kernel set1", 6),
                  ("bwd_kv_kernel set2", 6), ("bwd_q_kernel set2", 6)]
     else:
         calls = [("fwd_kernel", 4), ("bwd_kv_kernel fused set1", 8), ("bwd_kv_kernel fused set2", 8)]
-    dq = torch.empty(w.heads, w.n_q, d, device="cuda", dtype=torch.float32)
-    dk = torch.empty(w.heads, w.n_k, d, device="cuda", dtype=torch.float32)
+    grads = [torch.empty(w.heads, n, d, device="cuda", dtype=torch.float32) for n in (w.n_q, w.n_k, w.n_q, w.n_k)]
+    dq, dk = grads[0], grads[1]
 
     def step(ev=None):
         i = 0
@@ -499,6 +512,13 @@ def main():
         mark()
         kl, l1, l2 = skl.fwd(q1, k1, q2, k2, scale, causal)
         mark()
+        if path == "both":
+            dq1, dk1, dq2, dk2 = grads
+            skl.bwd_both(q1, k1, q2, k2, scale, causal, l1, l2, kl, path="dk_only", dk1=dk1, dk2=dk2)
+            mark()
+            skl.bwd_both(q1, k1, q2, k2, scale, causal, l1, l2, kl, path="dq_only", dq1=dq1, dq2=dq2)
+            mark()
+            return
         for setting in (1, 2):
             kw = dict(kl=kl) if setting == 2 else {}
             if path == "separate":
@@ -533,14 +553,18 @@ def main():
         parts[name] = {"ms": round(float(t), 3), "tflops": round(k * d * E / (t * 1e-3) / 1e12, 1),
                        "work": f"{k}*d flop per unmasked pair"}
     fwd_ms_ = float(mean_call[0])
-    bwd1_ms = float(mean_call[1:1 + (len(calls) - 1) // 2].sum())
-    bwd2_ms = float(mean_call[1 + (len(calls) - 1) // 2:].sum())
+    bwd_ms = float(mean_call[1:].sum())
     parts["fwd_ms"] = round(fwd_ms_, 3)
-    parts["bwd_set1_ms"] = round(bwd1_ms, 3)
-    parts["bwd_set2_ms"] = round(bwd2_ms, 3)
     parts["fwd_tflops"] = round(flop_fwd / (fwd_ms_ * 1e-3) / 1e12, 1)
-    parts["bwd_set1_tflops"] = round(flop_bwd / (bwd1_ms * 1e-3) / 1e12, 1)
-    parts["bwd_set2_tflops"] = round(flop_bwd / (bwd2_ms * 1e-3) / 1e12, 1)
+    parts["bwd_both_settings_ms"] = round(bwd_ms, 3)
+    parts["bwd_both_settings_tflops"] = round(2 * flop_bwd / (bwd_ms * 1e-3) / 1e12, 1)
+    if path != "both":
+        bwd1_ms = float(mean_call[1:1 + (len(calls) - 1) // 2].sum())
+        bwd2_ms = float(mean_call[1 + (len(calls) - 1) // 2:].sum())
+        parts["bwd_set1_ms"] = round(bwd1_ms, 3)
+        parts["bwd_set2_ms"] = round(bwd2_ms, 3)
+        parts["bwd_set1_tflops"] = round(flop_bwd / (bwd1_ms * 1e-3) / 1e12, 1)
+        parts["bwd_set2_tflops"] = round(flop_bwd / (bwd2_ms * 1e-3) / 1e12, 1)
     parts["pct_mfma_peak_step"] = round(100 * value / PEAK_BF16_TFLOPS, 2)
     parts["wall_s_timed"] = round(wall, 3)
     parts["upload_s"] = round(t_up, 1)

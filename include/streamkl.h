@@ -139,6 +139,26 @@ int streamkl_bwd_set2(const void* q1, const void* k1, const void* q2, const void
                       hipStream_t stream);
 
 /*
+ * Backward, both settings at once (Methodology 2, both gradient settings for
+ * the same loss sum_i g_i KL_i): writes Setting 2's dq1 = scale dS1 K1,
+ * dk1 = scale dS1^T Q1 and Setting 1's dq2 = scale dS2 K2, dk2 = scale dS2^T Q2
+ * (fp32, overwritten), from one recomputation of S1, S2 and P1 per
+ * (query, key) pair, where calling streamkl_bwd_set1 and streamkl_bwd_set2
+ * recomputes them twice.  kl, lse1, lse2 are the forward's outputs; dkl as
+ * for streamkl_bwd_set1 (NULL = all ones).  The four output arrays must not
+ * overlap.  bf16 runs dedicated kernels (a dK kernel and a dQ kernel, one
+ * wave per SIMD); fp32 runs the two settings' separate kernels one after the
+ * other.  path: AUTO or SEPARATE (all four gradients), DK_ONLY (dk1, dk2;
+ * dq1, dq2 untouched and may be NULL) or DQ_ONLY (dq1, dq2); FUSED is
+ * STREAMKL_ERR_UNSUPPORTED.  Needs no workspace.
+ */
+int streamkl_bwd_both(const void* q1, const void* k1, const void* q2, const void* k2,
+                      int n_q, int n_k, int heads, int head_dim, int causal, float scale,
+                      streamkl_dtype dtype, const float* lse1, const float* lse2,
+                      const float* kl, const float* dkl, float* dq1, float* dk1,
+                      float* dq2, float* dk2, streamkl_bwd_path path, hipStream_t stream);
+
+/*
  * Device workspace, in bytes, that an entry point needs:
  *   op 0 = streamkl_fwd_splitk (num_splits 0 = the automatic choice),
  *   op 1 = streamkl_bwd_set1, op 2 = streamkl_bwd_set2.

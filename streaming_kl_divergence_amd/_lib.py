@@ -13,7 +13,7 @@ ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_SCALE, ERR_WORKSPACE, ERR_HIP, ERR_ALI
 BF16, FP32 = 0, 1
 BWD_AUTO, BWD_FUSED, BWD_SEPARATE, BWD_DK_ONLY, BWD_DQ_ONLY = 0, 1, 2, 3, 4
 
-EXPORTS = ("streamkl_fwd", "streamkl_fwd_splitk", "streamkl_bwd_set1", "streamkl_bwd_set2",
+EXPORTS = ("streamkl_fwd", "streamkl_fwd_splitk", "streamkl_bwd_set1", "streamkl_bwd_set2", "streamkl_bwd_both",
            "streamkl_workspace_bytes", "streamkl_splitk_auto", "streamkl_bwd_select", "streamkl_strerror")
 
 _P = ctypes.c_void_p
@@ -27,6 +27,7 @@ _SIGS = {
     "streamkl_fwd_splitk": (_I, _IN + [_I, _P, _P, _P, _P, _Z, _P]),
     "streamkl_bwd_set1": (_I, _IN + [_P, _P, _P, _P, _P, _I, _P, _Z, _P]),
     "streamkl_bwd_set2": (_I, _IN + [_P, _P, _P, _P, _P, _P, _I, _P, _Z, _P]),
+    "streamkl_bwd_both": (_I, _IN + [_P, _P, _P, _P, _P, _P, _P, _P, _I, _P]),
     "streamkl_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "streamkl_splitk_auto": (_I, [_I, _I, _I, _I]),
     "streamkl_bwd_select": (_I, [_I, _I, _I, _I, _I]),

@@ -53,6 +53,11 @@ class _AttentionKL(torch.autograd.Function):
             if want_k:
                 grads[ik] = dk.to(k1.dtype)
 
+        if ctx.setting == "both" and all(need[:4]):
+            # all four gradients: one recomputation serves both settings
+            dq1, dk1, dq2, dk2 = ops.bwd_both(q1, k1, q2, k2, ctx.scale, ctx.causal, lse1, lse2, kl, dkl=g)
+            grads = [dq1.to(q1.dtype), dk1.to(k1.dtype), dq2.to(q2.dtype), dk2.to(k2.dtype)]
+            return grads[0], grads[1], grads[2], grads[3], None, None, None
         if ctx.setting in ("student", "both"):
             run(1, 2, 3)   # Setting 1: dQ2, dK2
         if ctx.setting in ("teacher", "both"):

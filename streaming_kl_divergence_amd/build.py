@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libstreamkl.so")
-SOURCES = ["fwd.hip", "bwd.hip", "api.cpp"]
+SOURCES = ["fwd.hip", "bwd.hip", "bwd_both.hip", "api.cpp"]
 ARCH = "gfx950"
 
 
@@ -39,7 +39,9 @@ def flags() -> list[str]:
 
 
 # MFMA results stay in VGPRs: the VALU reads every score, and a result in an
-# AGPR would cost one v_accvgpr_read per value
+# AGPR would cost one v_accvgpr_read per value.  The both-settings kernels
+# (bwd_both.hip) need more registers than the VGPRs hold and leave the choice
+# to the compiler, which puts their gradient accumulators in AGPRs.
 EXTRA = {"fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"], "bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 

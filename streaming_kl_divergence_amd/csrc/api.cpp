@@ -235,6 +235,42 @@ int streamkl_bwd_set2(const void* q1, const void* k1, const void* q2, const void
                     dq1, dk1, path, workspace, workspace_bytes, stream);
 }
 
+int streamkl_bwd_both(const void* q1, const void* k1, const void* q2, const void* k2, int n_q, int n_k,
+                      int heads, int head_dim, int causal, float scale, streamkl_dtype dtype,
+                      const float* lse1, const float* lse2, const float* kl, const float* dkl, float* dq1,
+                      float* dk1, float* dq2, float* dk2, streamkl_bwd_path path, hipStream_t stream) {
+  int st = check_common(q1, k1, q2, k2, n_q, n_k, heads, head_dim, causal, scale, (int)dtype);
+  if (st) return st;
+  if ((int)path < STREAMKL_BWD_AUTO || (int)path > STREAMKL_BWD_DQ_ONLY || path == STREAMKL_BWD_FUSED)
+    return STREAMKL_ERR_UNSUPPORTED;
+  const bool want_dq = path != STREAMKL_BWD_DK_ONLY, want_dk = path != STREAMKL_BWD_DQ_ONLY;
+  if (!lse1 || !lse2 || !kl || (want_dq && (!dq1 || !dq2)) || (want_dk && (!dk1 || !dk2))) return STREAMKL_ERR_NULL;
+  if ((want_dq && (!aligned16(dq1) || !aligned16(dq2))) || (want_dk && (!aligned16(dk1) || !aligned16(dk2))))
+    return STREAMKL_ERR_ALIGN;
+  skl::BwdParams p;
+  memset(&p, 0, sizeof(p));
+  p.q1 = (const char*)q1;
+  p.k1 = (const char*)k1;
+  p.q2 = (const char*)q2;
+  p.k2 = (const char*)k2;
+  p.n_q = n_q;
+  p.n_k = n_k;
+  p.heads = heads;
+  p.causal = causal ? 1 : 0;
+  p.scale = scale;
+  p.c = scale * 1.4426950408889634f;
+  p.lse1 = lse1;
+  p.lse2 = lse2;
+  p.kl = kl;
+  p.dkl = dkl;
+  p.dq = dq2;
+  p.dk = dk2;
+  p.dq1 = dq1;
+  p.dk1 = dk1;
+  p.dq_splits = dq_splits_for(n_q, n_k, heads);
+  return status_of(skl::launch_bwd_both(p, (int)dtype, head_dim, want_dk, want_dq, stream));
+}
+
 const char* streamkl_strerror(int status) {
   switch (status) {
     case STREAMKL_OK: return "ok";

@@ -34,18 +34,9 @@
 //     crossing the diagonal or a tail take the masked path.
 #include <type_traits>
 
-#include "common.hpp"
-#include "kernels.hpp"
+#include "bwd_shared.hpp"
 
 namespace skl {
-
-// ---- transposed LDS tiles ------------------------------------------------------
-// XT[d][j] (d < D, j < R) of element T; row stride R*sizeof(T) + PAD bytes.
-template <typename T, int D, int R, int PAD>
-struct TGeom {
-  static constexpr int kStride = R * (int)sizeof(T) + PAD;
-  static constexpr int kBytes = D * kStride;
-};
 
 // Write XT from row-major source rows, four rows at a time: `fetch(row, c)`
 // returns chunk c (16 bytes) of source row `row`.  NT threads share the work.
@@ -192,21 +183,6 @@ __device__ __forceinline__ float dlogit(float x1, float x2, float c, float a, fl
 }
 
 // ---- key-block kernel: dK (separate path) or dK + atomic dQ (fused path) ---------
-template <typename T, int D>
-struct KvCfg {
-  static constexpr int NW = 4;
-  static constexpr int BKW = 32 * NW;                                    // keys per workgroup
-  static constexpr int BT = (sizeof(T) == 4 && D == 128) ? 32 : 64;      // queries per tile
-  static constexpr int NQB = BT / 32;
-  static constexpr int TILE = BT * Geom<T, D>::kRowBytes;
-  static constexpr bool TR = sizeof(T) == 2;   // bf16: transposing reads; fp32: a transposed copy
-  using QT = TGeom<T, D, BT, 8>;
-  using KT = TGeom<T, D, BKW, 16>;
-  using DS = TGeom<T, BT, BKW, 16>;   // dS rows: [query][key]
-  static constexpr int kQtBytes = TR ? 0 : QT::kBytes;
-  static constexpr int kLdsBase = 4 * TILE + kQtBytes + 2 * 3 * BT * 4;
-  static constexpr int kLdsFused = kLdsBase + KT::kBytes + DS::kBytes;
-};
 
 // bf16 separate path: two waves per SIMD (256 VGPRs); the fp32 and fused
 // instantiations need more registers and run one wave per SIMD.
@@ -460,17 +436,6 @@ void bwd_kv_kernel(BwdParams p) {
 }
 
 // ---- query-block kernel: dQ of the separate path -----------------------------------
-template <typename T, int D>
-struct QCfg {
-  static constexpr int NW = 4;
-  static constexpr int BQ = 32 * NW;
-  static constexpr int BK = (sizeof(T) == 4 && D == 128) ? 32 : 64;
-  static constexpr int NKB = BK / 32;
-  static constexpr int TILE = BK * Geom<T, D>::kRowBytes;
-  static constexpr bool TR = sizeof(T) == 2;
-  using KT = TGeom<T, D, BK, 8>;
-  static constexpr int kLds = 4 * TILE + (TR ? 0 : KT::kBytes);
-};
 
 template <typename T, int D, int SETTING, bool SPLIT, bool HAS_G>
 __global__ __launch_bounds__(256) void bwd_q_kernel(BwdParams p) {
@@ -645,7 +610,7 @@ __global__ __launch_bounds__(256) void zero_fill_kernel(float4* p, size_t n4) {
 }
 
 // ---- launches ---------------------------------------------------------------------
-static hipError_t zero_fill(float* p, size_t n, hipStream_t s) {
+hipError_t zero_fill(float* p, size_t n, hipStream_t s) {
   // n is a multiple of 4 (head_dim is 64 or 128) and p is 16-byte aligned
   const size_t n4 = n / 4;
   const unsigned blocks = (unsigned)((n4 + 255) / 256 < 4096 ? (n4 + 255) / 256 : 4096);

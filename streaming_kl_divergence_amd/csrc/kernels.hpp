@@ -48,14 +48,21 @@ struct BwdParams {
   const float* lse2;
   const float* kl;    // Setting 2 only
   const float* dkl;   // NULL = all ones
-  float* dq;          // gradient of the setting's Q (fp32)
-  float* dk;          // gradient of the setting's K (fp32)
-  int setting;        // 1 or 2
+  float* dq;          // gradient of the setting's Q (fp32); both settings: dQ2
+  float* dk;          // gradient of the setting's K (fp32); both settings: dK2
+  float* dq1;         // both settings: dQ1 (Setting 2's gradients)
+  float* dk1;         // both settings: dK1
+  int setting;        // 1 or 2 (ignored by the both-settings launch)
   int dq_splits;      // separate path: key ranges of the dQ kernel (1 = plain stores)
 };
 
 hipError_t launch_bwd_separate(const BwdParams& p, int dtype, int head_dim, bool dk, bool dq, hipStream_t stream);
 hipError_t launch_bwd_fused(const BwdParams& p, int dtype, int head_dim, hipStream_t stream);
+// Both settings from one recomputation: dQ2, dK2 into p.dq, p.dk and dQ1, dK1
+// into p.dq1, p.dk1 (needs p.kl); dk / dq select the key-block and the
+// query-block kernel.  fp32 inputs run the two settings one after the other
+// on the separate kernels.
+hipError_t launch_bwd_both(const BwdParams& p, int dtype, int head_dim, bool dk, bool dq, hipStream_t stream);
 
 // Whether the fused kernel's LDS footprint fits a workgroup for this dtype and head_dim.
 bool fused_supported(int dtype, int head_dim);

@@ -105,3 +105,31 @@ def bwd(setting: int, q1, k1, q2, k2, scale: float, causal: bool, lse1, lse2, kl
         raise ValueError("setting must be 1 or 2")
     _lib.check(f"streamkl_bwd_set{setting}", st)
     return dq, dk
+
+
+def bwd_both(q1, k1, q2, k2, scale: float, causal: bool, lse1, lse2, kl, dkl=None, path: str = "auto", dq1=None,
+             dk1=None, dq2=None, dk2=None):
+    """(dQ1, dK1, dQ2, dK2), fp32: Setting 2's and Setting 1's gradients of the
+    same loss from one recomputation.  path: "auto"/"separate" (all four),
+    "dk_only" (dQ1, dQ2 returned as None) or "dq_only" (dK1, dK2 None).
+    Outputs may be given."""
+    heads, n_q, n_k, d, dt = _inputs(q1, k1, q2, k2)
+    if path not in ("auto", "separate", "dk_only", "dq_only"):
+        raise ValueError(f"unknown path {path!r}")
+    for t in (lse1, lse2, kl, dkl):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or t.shape != (heads, n_q)):
+            raise ValueError("lse1, lse2, kl, dkl must be contiguous fp32 [heads, n_q]")
+    if kl is None:
+        raise ValueError("the both-settings backward needs the forward's KL rows")
+    outs = []
+    for o, n, want in ((dq1, n_q, path != "dk_only"), (dk1, n_k, path != "dq_only"),
+                       (dq2, n_q, path != "dk_only"), (dk2, n_k, path != "dq_only")):
+        if o is None and want:
+            o = torch.empty(heads, n, d, device=q1.device, dtype=torch.float32)
+        outs.append(o if want else None)
+    L = _lib.lib()
+    st = L.streamkl_bwd_both(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), n_q, n_k, heads, d,
+                             int(causal), float(scale), dt, lse1.data_ptr(), lse2.data_ptr(), kl.data_ptr(),
+                             _ptr(dkl), *[_ptr(o) for o in outs], _PATH[path], _stream())
+    _lib.check("streamkl_bwd_both", st)
+    return tuple(outs)

@@ -92,6 +92,25 @@ def test_backward_validation():
     assert lib.streamkl_bwd_set2(*bad, FAKE, None, FAKE, FAKE, 0, None, 0, None) == L.ERR_SHAPE
 
 
+def test_both_settings_validation():
+    lib = L.lib()
+    base = [FAKE] * 4 + [16, 16, 2, 64, 1, 0.125, L.BF16, FAKE, FAKE]
+    # lse1 lse2 | kl dkl dq1 dk1 dq2 dk2 path stream
+    assert lib.streamkl_bwd_both(*base, None, None, FAKE, FAKE, FAKE, FAKE, 0, None) == L.ERR_NULL   # kl
+    assert lib.streamkl_bwd_both(*base, FAKE, None, FAKE, FAKE, None, FAKE, 0, None) == L.ERR_NULL   # dq2
+    assert lib.streamkl_bwd_both(*base, FAKE, None, FAKE, FAKE + 8, FAKE, FAKE, 0, None) == L.ERR_ALIGN
+    assert lib.streamkl_bwd_both(*base, FAKE, None, FAKE, FAKE, FAKE, FAKE, L.BWD_FUSED, None) == L.ERR_UNSUPPORTED
+    assert lib.streamkl_bwd_both(*base, FAKE, None, FAKE, FAKE, FAKE, FAKE, 9, None) == L.ERR_UNSUPPORTED
+    # DK_ONLY needs no dQ outputs; DQ_ONLY no dK outputs (these checks stop before any launch: bad head_dim)
+    bad = list(base)
+    bad[7] = 96  # head_dim
+    assert lib.streamkl_bwd_both(*bad, FAKE, None, None, FAKE, None, FAKE, L.BWD_DK_ONLY, None) == L.ERR_UNSUPPORTED
+    assert lib.streamkl_bwd_both(*bad, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None) == L.ERR_UNSUPPORTED
+    bad = list(base)
+    bad[9] = float("nan")
+    assert lib.streamkl_bwd_both(*bad, FAKE, None, FAKE, FAKE, FAKE, FAKE, 0, None) == L.ERR_SCALE
+
+
 def test_strerror_covers_every_code():
     lib = L.lib()
     for code in (L.OK, L.ERR_NULL, L.ERR_SHAPE, L.ERR_UNSUPPORTED, L.ERR_SCALE, L.ERR_WORKSPACE, L.ERR_HIP,

@@ -1,0 +1,72 @@
+"""GPU backward of both settings from one recomputation (streamkl_bwd_both)
+against the fp64 oracle, and against the two single-setting launches."""
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import device_inputs, log, need_gpu
+from tests.parity import bf16_ds_bound, compare
+from tests.test_gpu_backward import BWD_EDGE
+from tests.test_gpu_forward import _rand_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _both(dev, scale, causal, g=None):
+    import torch
+    import streaming_kl_divergence_amd as skl
+    kl, l1, l2 = skl.fwd(*dev, scale, causal)
+    dkl = None if g is None else torch.from_numpy(np.ascontiguousarray(g, dtype=np.float32)).cuda()
+    out = skl.bwd_both(*dev, scale, causal, l1, l2, kl, dkl=dkl)
+    torch.cuda.synchronize()
+    return [o.cpu().numpy() for o in out], (kl, l1, l2, dkl)
+
+
+@pytest.mark.parametrize("with_g", [False, True])
+@pytest.mark.parametrize("idx", range(len(BWD_EDGE)), ids=[str(c) for c in BWD_EDGE])
+def test_edge_shapes(idx, with_g):
+    need_gpu()
+    case = BWD_EDGE[idx]
+    heads, n_q, n_k, d, dtype, causal, sm = case
+    log(f"case both {case} g={with_g}")
+    arrs = _rand_case(200 + idx, heads, n_q, n_k, d, dtype, corr=(sm != 4.0))
+    g = np.random.default_rng(300 + idx).uniform(0.5, 1.5, (heads, n_q)).astype(np.float32) if with_g else None
+    scale = sm / np.sqrt(d)
+    (dq1, dk1, dq2, dk2), _ = _both(device_inputs(arrs, dtype), scale, causal, g)
+    derived = sm != 1.0 and dtype == "bf16"
+    for setting, (dq, dk) in ((1, (dq2, dk2)), (2, (dq1, dk1))):
+        rdq, rdk = oracle.backward(setting, *arrs, scale, causal, dkl=g)
+        eq = ek = None
+        if derived:
+            eq, ek = bf16_ds_bound(oracle, setting, arrs, scale, causal, g)
+        compare(dq, rdq, dtype, f"{case} setting {setting} dq", extra_abs=eq)
+        compare(dk, rdk, dtype, f"{case} setting {setting} dk", extra_abs=ek)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_matches_single_setting_launches(causal):
+    """The same per-pair arithmetic and accumulation order as the dK-only and
+    dQ-only kernels of each setting: equal up to fp32 reassociation."""
+    need_gpu()
+    import torch
+    import streaming_kl_divergence_amd as skl
+    arrs = _rand_case(23, 2, 700, 1500 if not causal else 700, 128, "bf16")
+    dev = device_inputs(arrs, "bf16")
+    g = np.random.default_rng(5).uniform(0.5, 1.5, (2, 700)).astype(np.float32)
+    both, (kl, l1, l2, dkl) = _both(dev, 0.09, causal, g)
+    for setting, ref in ((1, both[2:]), (2, both[:2])):
+        kw = dict(kl=kl) if setting == 2 else {}
+        dq, dk = skl.bwd(setting, *dev, 0.09, causal, l1, l2, dkl=dkl, path="separate", **kw)
+        torch.cuda.synchronize()
+        for a, b, n in ((ref[0], dq.cpu().numpy(), "dq"), (ref[1], dk.cpu().numpy(), "dk")):
+            assert np.abs(a - b).max() <= 1e-5 * np.abs(b).max(), f"setting {setting} {n}"
+
+
+def test_rejects_missing_kl():
+    need_gpu()
+    import streaming_kl_divergence_amd as skl
+    arrs = _rand_case(24, 1, 64, 64, 64, "bf16")
+    dev = device_inputs(arrs, "bf16")
+    kl, l1, l2 = skl.fwd(*dev, 0.125, False)
+    with pytest.raises(ValueError):
+        skl.bwd_both(*dev, 0.125, False, l1, l2, None)

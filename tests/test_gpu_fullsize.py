@@ -7,7 +7,8 @@ configuration the benchmark times.
   backward settings through the dK-only and dQ-only launches: dQ on sampled
   rows of heads 0 and 31, dK on sampled keys of head 0 (from the oracle's own
   per-row statistics of that head), and on every head the identities
-  sum_j dK_j = 0 and sum_i q_i . dQ_i = sum_j k_j . dK_j.
+  sum_j dK_j = 0 and sum_i q_i . dQ_i = sum_j k_j . dK_j; the both-settings
+  launches (the benchmark's) against those, element by element.
 * 512K-key decode (32 heads, one query): split-K with the automatic split count
   and with explicit counts, and the single-pass kernel, all heads.
 * 128K non-causal (32 heads): forward on sampled rows of every head; Setting 2
@@ -94,6 +95,13 @@ def causal64k():
         skl.bwd(setting, q1, k1, q2, k2, w.scale, w.causal, l1, l2, path="dk_only", dk=dk, **kw)
         skl.bwd(setting, q1, k1, q2, k2, w.scale, w.causal, l1, l2, path="dq_only", dq=dq, **kw)
         grads[setting] = (dq, dk)
+    # the benchmark's launches: both settings from one recomputation, dK kernel then dQ kernel
+    dq1, dk1, dq2, dk2 = [torch.empty(w.heads, n, w.head_dim, device="cuda", dtype=torch.float32)
+                          for n in (w.n_q, w.n_k, w.n_q, w.n_k)]
+    skl.bwd_both(q1, k1, q2, k2, w.scale, w.causal, l1, l2, kl, path="dk_only", dk1=dk1, dk2=dk2)
+    skl.bwd_both(q1, k1, q2, k2, w.scale, w.causal, l1, l2, kl, path="dq_only", dq1=dq1, dq2=dq2)
+    grads["both1"] = (dq2, dk2)
+    grads["both2"] = (dq1, dk1)
     torch.cuda.synchronize()
     log("causal64k: GPU done; oracle head 0 (all rows)")
     a0 = head64(w, 0)
@@ -124,6 +132,11 @@ def test_causal64k_forward(causal64k):
 def test_causal64k_backward(causal64k, setting):
     w, dev, _, grads, a0, state0 = causal64k
     dq, dk = grads[setting]
+    # the both-settings launches: the same per-pair arithmetic and accumulation
+    # order as the single-setting kernels
+    for a, b, n in ((grads[f"both{setting}"][0], dq, "dq"), (grads[f"both{setting}"][1], dk, "dk")):
+        diff = float((a - b).abs().max())
+        assert diff <= 1e-5 * float(b.abs().max()), f"both-settings {n} differs from setting {setting}: {diff}"
     q_t, k_t = (dev[2], dev[3]) if setting == 1 else (dev[0], dev[1])
     _identities(q_t, k_t, dq, dk, f"causal64k setting {setting}")
     rng = np.random.default_rng(30 + setting)

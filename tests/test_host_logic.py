@@ -66,6 +66,8 @@ def test_kernel_labels():
     assert L("_ZN3skl13bwd_kv_kernelIDF16bLi128ELi2ELb1ELb0EEEvNS_9BwdParamsE") == "bwd_kv_kernel fused set2"
     assert L("_ZN3skl12bwd_q_kernelIDF16bLi128ELi2ELb0ELb1EEEvNS_9BwdParamsE") == "bwd_q_kernel set2"
     assert L("_ZN3skl21splitk_combine_kernelENS_9FwdParamsE") == "splitk_combine_kernel"
+    assert L("_ZN3skl18bwd_kv_both_kernelILi128ELb0EEEvNS_9BwdParamsE") == "bwd_kv_both_kernel"
+    assert L("_ZN3skl17bwd_q_both_kernelILi128ELb0ELb1EEEvNS_9BwdParamsE") == "bwd_q_both_kernel"
     assert L("__amd_rocclr_copyBuffer") is None
 
 
