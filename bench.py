@@ -101,18 +101,28 @@ def measured_traffic(kernel: str):
     return e.get("bytes_per_launch")
 
 
+_KERNELS = "fwd_kernel|bwd_kv_kernel|bwd_q_kernel|bwd_kv_both_kernel|bwd_q_both_kernel|splitk_combine_kernel"
+
+
 def kernel_label(symbol: str):
-    """Benchmark label of a library kernel symbol (None for other kernels)."""
+    """Benchmark label of a library kernel symbol, mangled or demangled (None
+    for other kernels)."""
     import re
-    m = re.match(r"_ZN3skl(\d+)(fwd_kernel|bwd_kv_kernel|bwd_q_kernel|bwd_kv_both_kernel|bwd_q_both_kernel|"
-                 r"splitk_combine_kernel)(.*)$", symbol)
-    if not m:
-        return None
-    name, targs = m.group(2), m.group(3)
+    m = re.match(r"_ZN3skl(\d+)(" + _KERNELS + r")(.*)$", symbol)
+    if m:
+        name, targs = m.group(2), m.group(3)
+        st = re.search(r"Li\d+ELi(\d)ELb(\d)", targs)
+        setting, flag = (st.group(1), st.group(2)) if st else ("?", "0")
+    else:
+        m = re.match(r"(?:void )?skl::(" + _KERNELS + r")(?:<([^>]*)>)?\(", symbol)
+        if not m:
+            return None
+        name = m.group(1)
+        targs = [a.strip() for a in (m.group(2) or "").split(",")]
+        # single-setting kernels: <T, D, SETTING, FUSED or SPLIT, HAS_G>
+        setting, flag = (targs[2], "1" if targs[3] == "true" else "0") if len(targs) >= 4 else ("?", "0")
     if name in ("fwd_kernel", "splitk_combine_kernel", "bwd_kv_both_kernel", "bwd_q_both_kernel"):
         return name
-    st = re.search(r"Li\d+ELi(\d)ELb(\d)", targs)
-    setting, flag = (st.group(1), st.group(2)) if st else ("?", "0")
     fused = name == "bwd_kv_kernel" and flag == "1"
     return f"{name}{' fused' if fused else ''} set{setting}"
 

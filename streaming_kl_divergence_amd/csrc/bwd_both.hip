@@ -6,9 +6,11 @@
 // each recomputing P from the saved LSEs.  When both are wanted, one
 // recomputation of S1, S2 and P1 per (query, key) pair serves the two.
 //
-// Compiled without the VGPR-only MFMA form: the two settings' gradient
-// accumulators live in the accumulation registers (AGPRs) next to the scores
-// in VGPRs, which is what lets one wave hold both.
+// Compiled without the VGPR-only MFMA form: MFMA results go to the
+// accumulation registers (AGPRs; the scores are read back with one
+// v_accvgpr_read per value), which leaves the VGPRs to the resident operand
+// rows and the dS work, so that both settings' gradient accumulators fit one
+// wave.
 #include "bwd_shared.hpp"
 
 namespace skl {
@@ -59,7 +61,9 @@ void bwd_kv_both_kernel(BwdParams p) {
   using T = __bf16;
   using G = Geom<T, D>;
   using C = KvCfg<T, D>;
-  constexpr int NW = C::NW, BT = C::BT, NQB = C::NQB, TILE = C::TILE, DB = D / 32;
+  // 128-query tiles (twice the single-setting kernel's): one workgroup per CU
+  // holds them double-buffered, and each barrier and tile copy covers more work
+  constexpr int NW = C::NW, BT = 2 * C::BT, NQB = 2 * C::NQB, TILE = 2 * C::TILE, DB = D / 32;
   constexpr int NC = 4;   // per-row arrays in LDS: a, b, c3, g
   __shared__ __attribute__((aligned(16))) char smem[4 * TILE + 2 * NC * BT * 4];
   SKL_LDS char* lds = (SKL_LDS char*)smem;
@@ -237,7 +241,8 @@ void bwd_q_both_kernel(BwdParams p) {
   using T = __bf16;
   using G = Geom<T, D>;
   using C = QCfg<T, D>;
-  constexpr int NW = C::NW, BQ = C::BQ, BK = C::BK, NKB = C::NKB, TILE = C::TILE, DB = D / 32;
+  // 128-key tiles, as in the key-block kernel above
+  constexpr int NW = C::NW, BQ = C::BQ, BK = 2 * C::BK, NKB = 2 * C::NKB, TILE = 2 * C::TILE, DB = D / 32;
   __shared__ __attribute__((aligned(16))) char smem[4 * TILE];
   SKL_LDS char* lds = (SKL_LDS char*)smem;
 

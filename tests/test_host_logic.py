@@ -68,6 +68,13 @@ def test_kernel_labels():
     assert L("_ZN3skl21splitk_combine_kernelENS_9FwdParamsE") == "splitk_combine_kernel"
     assert L("_ZN3skl18bwd_kv_both_kernelILi128ELb0EEEvNS_9BwdParamsE") == "bwd_kv_both_kernel"
     assert L("_ZN3skl17bwd_q_both_kernelILi128ELb0ELb1EEEvNS_9BwdParamsE") == "bwd_q_both_kernel"
+    # the profiler prints some names demangled
+    assert L("void skl::bwd_kv_both_kernel<128, false>(skl::BwdParams)") == "bwd_kv_both_kernel"
+    assert L("void skl::bwd_q_both_kernel<64, true, false>(skl::BwdParams)") == "bwd_q_both_kernel"
+    assert L("void skl::bwd_kv_kernel<__bf16, 128, 2, true, false>(skl::BwdParams)") == "bwd_kv_kernel fused set2"
+    assert L("void skl::bwd_q_kernel<__bf16, 128, 1, false, true>(skl::BwdParams)") == "bwd_q_kernel set1"
+    assert L("void skl::fwd_kernel<__bf16, 128, 4, false>(skl::FwdParams)") == "fwd_kernel"
+    assert L("skl::splitk_combine_kernel(skl::FwdParams)") == "splitk_combine_kernel"
     assert L("__amd_rocclr_copyBuffer") is None
 
 
