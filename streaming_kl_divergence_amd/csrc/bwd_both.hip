@@ -53,6 +53,41 @@ __device__ __forceinline__ void dlogit_both(float x1, float x2, float c, float s
   d1 = p1 * fmaf(HAS_G ? g * scale : scale, x1 - x2, c3);
 }
 
+// The transposing reads of one 32-row block's gradient operands for both
+// settings (tile ta for acca, tbt for accb), issued ahead of use.
+template <int D>
+struct GradOps {
+  u32x2 a[2][D / 32][2], b[2][D / 32][2];
+  __device__ __forceinline__ void load(const SKL_LDS char* ta, const SKL_LDS char* tbt, int rbase, const int* tb) {
+    constexpr int RB = D * 2;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int o = (rbase + 16 * t) * RB;
+        a[t][db][0] = read_tr4_at(ta + o + (tb[0] ^ (64 * db)));
+        a[t][db][1] = read_tr4_at(ta + o + (tb[1] ^ (64 * db)));
+        b[t][db][0] = read_tr4_at(tbt + o + (tb[0] ^ (64 * db)));
+        b[t][db][1] = read_tr4_at(tbt + o + (tb[1] ^ (64 * db)));
+      }
+  }
+  __device__ __forceinline__ void run(const PackedDS& pa, const PackedDS& pbk, f32x16* acca, f32x16* accb) const {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        acca[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, u32x4{a[t][db][0].x, a[t][db][0].y, a[t][db][1].x, a[t][db][1].y}), pa.b[t],
+            acca[db], 0, 0, 0);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+        accb[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, u32x4{b[t][db][0].x, b[t][db][0].y, b[t][db][1].x, b[t][db][1].y}), pbk.b[t],
+            accb[db], 0, 0, 0);
+    }
+  }
+};
+
 // Key-block kernel, both settings: dK2 = scale dS2^T Q2 and dK1 = scale dS1^T Q1
 // for this workgroup's 128 keys (the layout of bwd_kv_kernel, one wave per SIMD).
 template <int D, bool HAS_G>
@@ -168,6 +203,9 @@ void bwd_kv_both_kernel(BwdParams p) {
     if (wave_idle || (p.causal && kw0 > qlast + off)) return;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
+      GradOps<D> go;
+      go.load(t2, t1, qb * 32, tb);
+      __builtin_amdgcn_sched_barrier(0);
       f32x16 s1 = f32x16{}, s2 = f32x16{};
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -204,10 +242,7 @@ void bwd_kv_both_kernel(BwdParams p) {
       }
       // dK2^T += Q2^T dS2, dK1^T += Q1^T dS1
       const PackedDS pd2 = pack_ds(d2), pd1 = pack_ds(d1);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) dk2t[db] = kgroup_mfma_tr_packed<D>(t2, qb * 32, db, tb, pd2, dk2t[db]);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) dk1t[db] = kgroup_mfma_tr_packed<D>(t1, qb * 32, db, tb, pd1, dk1t[db]);
+      go.run(pd2, pd1, dk2t, dk1t);
     }
   };
   settle_scalar_loads();
@@ -347,6 +382,9 @@ void bwd_q_both_kernel(BwdParams p) {
     const int k0 = kbeg + t * BK;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
+      GradOps<D> go;
+      go.load(t2, t1, kb * 32, tb);
+      __builtin_amdgcn_sched_barrier(0);
       f32x16 s1 = f32x16{}, s2 = f32x16{};
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -373,10 +411,7 @@ void bwd_q_both_kernel(BwdParams p) {
       }
       // dQ2^T += K2^T dS2^T, dQ1^T += K1^T dS1^T
       const PackedDS pd2 = pack_ds(d2), pd1 = pack_ds(d1);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) dq2t[db] = kgroup_mfma_tr_packed<D>(t2, kb * 32, db, tb, pd2, dq2t[db]);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) dq1t[db] = kgroup_mfma_tr_packed<D>(t1, kb * 32, db, tb, pd1, dq1t[db]);
+      go.run(pd2, pd1, dq2t, dq1t);
     }
   };
   settle_scalar_loads();
