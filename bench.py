@@ -20,8 +20,9 @@ Usage:
       the one-line benchmark of the 64K causal step (the default).
   python bench.py --configs
       one JSON line per workload (tiny fp32, 8K causal, 64K causal with both
-      backward paths, 512K decode split-K vs single pass, 128K non-causal,
-      512 x 128K fused vs separate): median and min of timed runs per call.
+      backward paths and the both-settings backward, 512K decode split-K vs
+      single pass, 128K non-causal, 512 x 128K fused vs separate): median and
+      min of timed runs per call.
   python bench.py --sweep crossover|splitk|context
       the ablations: fused vs separate backward over N_Q at N_K = 128K; split-K
       vs one pass (and several split counts) over small N_Q; and latency,
@@ -267,13 +268,18 @@ def configs_mode():
             e.update({"gbs": round(float(gbs), 1), "pct_hbm": round(100 * float(gbs) / PEAK_HBM_GBS, 1)})
         return e
 
-    def run(name, settings, paths=("auto",), reps=10):
+    def run(name, settings, paths=("auto",), reps=10, both=False, splitk=False):
         w = W.WORKLOADS[name]
         q1, k1, q2, k2 = upload(w, threads)
         d, E = w.head_dim, w.elements()
         kl, l1, l2 = skl.fwd(q1, k1, q2, k2, w.scale, w.causal)
         rows = {"fwd": entry(_timed(lambda: skl.fwd(q1, k1, q2, k2, w.scale, w.causal), stream, 3, reps),
                              4 * d * E)}
+        if splitk:
+            # few query blocks: the split-K forward fills the chip
+            auto = skl.splitk_auto(w.n_q, w.n_k, w.heads, d)
+            rows[f"fwd splitk (auto {auto})"] = entry(
+                _timed(lambda: skl.fwd_splitk(q1, k1, q2, k2, w.scale, w.causal), stream, 3, reps), 4 * d * E)
         dq = torch.empty(w.heads, w.n_q, d, device="cuda", dtype=torch.float32)
         dk = torch.empty(w.heads, w.n_k, d, device="cuda", dtype=torch.float32)
         for st in settings:
@@ -283,13 +289,19 @@ def configs_mode():
                 ms = _timed(lambda: skl.bwd(st, q1, k1, q2, k2, w.scale, w.causal, l1, l2, path=path,
                                             dq=dq, dk=dk, **kw), stream, 3, reps)
                 rows[f"bwd set{st} {path}" + (f" ({chosen})" if path == "auto" else "")] = entry(ms, 8 * d * E)
+        if both:
+            outs = [torch.empty(w.heads, n, d, device="cuda", dtype=torch.float32) for n in (w.n_q, w.n_k, w.n_q, w.n_k)]
+            ms = _timed(lambda: skl.bwd_both(q1, k1, q2, k2, w.scale, w.causal, l1, l2, kl, dq1=outs[0], dk1=outs[1],
+                                             dq2=outs[2], dk2=outs[3]), stream, 3, reps)
+            rows["bwd both settings"] = entry(ms, 16 * d * E)
+            del outs
         line(w, rows)
         del q1, k1, q2, k2, dq, dk
         torch.cuda.empty_cache()
 
-    run("tiny", (1, 2))
+    run("tiny", (1, 2), both=True)
     run("causal8k", (1,))
-    run("causal64k", (1, 2), paths=("auto", "fused", "separate"), reps=5)
+    run("causal64k", (1, 2), paths=("auto", "fused", "separate"), reps=5, both=True)
     # decode: the same fused key loop with one split vs split-K
     w = W.WORKLOADS["decode512k"]
     q1, k1, q2, k2 = upload(w, threads)
@@ -305,7 +317,7 @@ def configs_mode():
     del q1, k1, q2, k2
     torch.cuda.empty_cache()
     run("noncausal128k", (2,), reps=3)
-    run("smallq128k", (2,), paths=("auto", "fused", "separate"))
+    run("smallq128k", (2,), paths=("auto", "fused", "separate"), splitk=True)
 
 
 def _rand_inputs(heads, n_q, n_k, d, seed=0, corr=True):
