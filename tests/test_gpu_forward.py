@@ -67,6 +67,11 @@ EDGE = [
     (2, 500, 640, 128, "bf16", False, 0.0),      # scale 0: uniform rows, KL = 0
     (2, 400, 900, 128, "bf16", True, 4.0),       # large logits (4 / sqrt(d))
     (1, 64, 64, 128, "bf16", True, 1.0),         # exactly one tile
+    (2, 32, 3000, 128, "bf16", False, 1.0),      # one-wave workgroups, many key tiles
+    (3, 17, 2049, 64, "bf16", True, 1.0),        # one-wave, causal bottom-right, ragged
+    (2, 5, 40, 128, "bf16", False, 1.0),         # one-wave, a single partial key tile
+    (2, 1, 300, 64, "fp32", False, 1.0),         # one query, fp32
+    (3, 1, 1, 128, "bf16", True, 1.0),           # one query, one key
 ]
 
 
@@ -117,6 +122,10 @@ def test_splitk_matches_oracle(splits):
     _check_all_rows(arrs, "bf16", 1 / np.sqrt(128), False, splits=splits, name=f"splits={splits}")
     arrs = _rand_case(12, 2, 200, 1000, 128, "bf16")
     _check_all_rows(arrs, "bf16", 1 / np.sqrt(128), True, splits=splits, name=f"causal splits={splits}")
+    # one-wave workgroups: key ranges of a few tiles each, the last one ragged
+    arrs = _rand_case(15, 2, 8, 3001, 128, "bf16")
+    for causal in (False, True):
+        _check_all_rows(arrs, "bf16", 1 / np.sqrt(128), causal, splits=splits, name=f"8 queries causal={causal} splits={splits}")
 
 
 def test_splitk_equals_fused():
