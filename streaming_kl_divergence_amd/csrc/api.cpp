@@ -6,6 +6,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "kernels.hpp"
 #include "streamkl.h"
 
@@ -14,16 +16,17 @@ namespace {
 constexpr int kMaxSplits = 1024;
 
 int device_cus() {
-  // Compute units of the current device (cached per device id, 64 devices).
-  static int cache[64] = {0};
+  // Compute units of the current device (cached per device id, 64 devices;
+  // racing first calls store the same value).
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
