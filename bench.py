@@ -81,10 +81,14 @@ def upload(w: W.Workload, threads: int):
 
 
 def kernel_source_hash() -> str:
+    """Hash of the device code (the .hip and .hpp files); host-only files such
+    as the C ABI's argument checks do not change what a kernel moves."""
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "streaming_kl_divergence_amd", "csrc"))):
-        with open(os.path.join(ROOT, "streaming_kl_divergence_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    csrc = os.path.join(ROOT, "streaming_kl_divergence_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(fh.read())
     return h.hexdigest()[:16]
 
 
