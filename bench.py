@@ -15,8 +15,12 @@ dK products, 4 d).  The both-settings kernels execute exactly this work (8 d
 per pair each); the single-setting path executes 12 d per setting, its second
 recomputation not counted.
 
+Beside the published peak, the line carries a measured one: a 16384^3 bf16
+GEMM through torch.mm (hipBLASLt) on the same GPU (parts.gemm_bf16_16384_tflops;
+--no-gemm-ref skips it).
+
 Usage:
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-gemm-ref]
       the one-line benchmark of the 64K causal step (the default).
   python bench.py --configs
       one JSON line per workload (tiny fp32, 8K causal, 64K causal with both
@@ -35,7 +39,7 @@ Usage:
       reads two rocprofv3 --pmc outputs (FETCH_SIZE, then WRITE_SIZE, both of a
       --copy-calibration run), scales each counter by what it reads for the
       1 GiB copy, and writes profiles/traffic.json (HBM bytes per launch per
-      kernel, tagged with a hash of the kernel sources).
+      kernel, tagged with a hash of the device sources).
   python bench.py --sq-summary DIR [DIR ...]
       reads rocprofv3 --pmc outputs holding SQ counters and GRBM_GUI_ACTIVE
       and prints, per kernel, how busy the matrix cores, the vector ALU and
@@ -457,12 +461,26 @@ def cpu_baseline():
                       f"Setting 2, fp64 numpy/BLAS; {dt:.1f} s for {flop / 1e12:.3f} TFLOP"}
 
 
+def gemm_reference(n: int = 16384, reps: int = 10) -> float:
+    """Dense bf16 GEMM throughput of the platform library (torch.mm, which
+    calls hipBLASLt) on this GPU, TFLOP/s: a measured reference for what the
+    matrix cores deliver on a plain contraction, beside the published peak."""
+    import torch
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    t = _timed(lambda: torch.mm(a, b, out=c), torch.cuda.current_stream(), 3, reps)
+    del a, b, c
+    return 2.0 * n ** 3 / (float(np.median(t)) * 1e-3) / 1e12
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gemm-ref", action="store_true", help="skip the bf16 GEMM reference measurement")
     ap.add_argument("--workload", default="causal64k")
     ap.add_argument("--configs", action="store_true")
     ap.add_argument("--sweep", choices=("crossover", "splitk", "context"))
@@ -592,6 +610,10 @@ def main():
         parts["bwd_set1_tflops"] = round(flop_bwd / (bwd1_ms * 1e-3) / 1e12, 1)
         parts["bwd_set2_tflops"] = round(flop_bwd / (bwd2_ms * 1e-3) / 1e12, 1)
     parts["pct_mfma_peak_step"] = round(100 * value / PEAK_BF16_TFLOPS, 2)
+    if not args.no_gemm_ref:
+        gemm = gemm_reference()
+        parts["gemm_bf16_16384_tflops"] = round(gemm, 1)
+        parts["pct_of_gemm_step"] = round(100 * value / gemm, 1)
     parts["wall_s_timed"] = round(wall, 3)
     parts["upload_s"] = round(t_up, 1)
 
