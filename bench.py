@@ -35,11 +35,15 @@ Usage:
   python bench.py --copy-calibration ...
       also runs one plain 1 GiB device copy first, so that a rocprofv3 --pmc
       run sees FETCH_SIZE / WRITE_SIZE of a copy of known size.
-  python bench.py --pmc-summary FETCH_DIR WRITE_DIR
+  python bench.py --workload decode512k
+      the decode line instead: the split-K forward for one query per head,
+      rated in GB/s against the HBM peak.
+  python bench.py --pmc-summary FETCH_DIR WRITE_DIR [--workload NAME]
       reads two rocprofv3 --pmc outputs (FETCH_SIZE, then WRITE_SIZE, both of a
       --copy-calibration run), scales each counter by what it reads for the
-      1 GiB copy, and writes profiles/traffic.json (HBM bytes per launch per
-      kernel, tagged with a hash of the device sources).
+      1 GiB copy, and writes profiles/traffic.json (profiles/traffic_NAME.json
+      for another workload: HBM bytes per launch per kernel, tagged with a hash
+      of the device sources).
   python bench.py --sq-summary DIR [DIR ...]
       reads rocprofv3 --pmc outputs holding SQ counters and GRBM_GUI_ACTIVE
       and prints, per kernel, how busy the matrix cores, the vector ALU and
@@ -96,10 +100,16 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str):
+def traffic_path(workload: str = "causal64k") -> str:
+    """The committed counter summary of a workload's bench run."""
+    name = "traffic.json" if workload == "causal64k" else f"traffic_{workload}.json"
+    return os.path.join(ROOT, "profiles", name)
+
+
+def measured_traffic(kernel: str, workload: str = "causal64k"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None if there is none or the kernel sources changed since it was taken."""
-    p = os.path.join(ROOT, "profiles", "traffic.json")
+    p = traffic_path(workload)
     if not os.path.exists(p):
         return None
     with open(p) as f:
@@ -139,7 +149,7 @@ def kernel_label(symbol: str):
 COPY_BYTES = 1 << 30
 
 
-def pmc_summary(fetch_dir: str, write_dir: str):
+def pmc_summary(fetch_dir: str, write_dir: str, workload: str = "causal64k"):
     """HBM bytes per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
     each scaled by the ratio of the 1 GiB copy's true bytes to what the
     counter reads for it."""
@@ -181,7 +191,7 @@ def pmc_summary(fetch_dir: str, write_dir: str):
         wb = w_factor * float(np.mean(write.get(name, [0.0])))
         table[label] = {"symbol": name, "dispatches": len(v), "fetch_bytes": round(fb), "write_bytes": round(wb),
                         "bytes_per_launch": round(fb + wb), "source_hash": h}
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = traffic_path(workload)
     with open(path, "w") as f:
         json.dump(table, f, indent=1, sort_keys=True)
     print(json.dumps(table, indent=1, sort_keys=True))
@@ -461,6 +471,70 @@ def cpu_baseline():
                       f"Setting 2, fp64 numpy/BLAS; {dt:.1f} s for {flop / 1e12:.3f} TFLOP"}
 
 
+def decode_mode(w: W.Workload, args, inputs, t_up: float):
+    """One query per head (decode): one step is the split-K forward with the
+    library's automatic split count, the partial kernel and then the combine
+    kernel (a few microseconds).  Bound by HBM: the rate is the bytes of
+    K1, K2, Q1, Q2 read once per step over the step's time."""
+    import torch
+    import streaming_kl_divergence_amd as skl
+    q1, k1, q2, k2 = inputs
+    d = w.head_dim
+    stream = torch.cuda.current_stream()
+    splits = skl.splitk_auto(w.n_q, w.n_k, w.heads, d)
+    ws = torch.empty(max(16, skl.splitk_workspace_bytes(w.n_q, w.n_k, w.heads, d, 0)), device="cuda",
+                     dtype=torch.uint8)
+    call = lambda: skl.fwd_splitk(q1, k1, q2, k2, w.scale, w.causal, 0, ws)
+    t = _timed(call, stream, args.warmup, args.steps)
+    ms = float(np.mean(t))
+    esize = 2 if w.dtype == "bf16" else 4
+    byts = 2 * w.heads * (w.n_k + w.n_q) * d * esize
+    gbs = byts / (ms * 1e-3) / 1e9
+    out = {
+        "metric": f"split-K decode HBM read rate ({w.heads} heads, N_Q={w.n_q}, N_K={w.n_k}, d={d}, {w.dtype})",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.heads} heads, N_Q={w.n_q}, N_K={w.n_k}, head_dim={d}, {w.dtype}, "
+                               f"non-causal, independent teacher and student; step = split-K forward",
+                   "heads": w.heads, "n_q": w.n_q, "n_k": w.n_k, "head_dim": d, "causal": w.causal,
+                   "splits": splits},
+        "parts": {"upload_s": round(t_up, 1), "min_ms": round(float(t.min()), 4)},
+        "roofline": {"bound": "hbm", "kernel": "fwd_kernel (split-K partials; the timed call includes the combine)",
+                     "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("fwd_kernel", w.name),
+                     "avg_launch_ms": round(ms, 4),
+                     "work_per_launch": f"K1, K2, Q1, Q2 read once = {byts} bytes"},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_decode(w)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline_decode(w: W.Workload, heads: int = 0):
+    """The fp64 oracle's forward on the first `heads` heads (0 = all) of a
+    decode workload (each head's one query against all its keys), as the
+    same bytes-per-second rate; inputs are drawn before the clock starts."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    heads = heads or w.heads
+    dt = 0.0
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        for a in ex.map(lambda h: W.head_inputs(w, h), range(heads)):
+            t0 = time.perf_counter()
+            oracle.forward_head(*a, w.scale, w.causal)
+            dt += time.perf_counter() - t0
+    esize = 2 if w.dtype == "bf16" else 4
+    byts = heads * 2 * (w.n_k + w.n_q) * w.head_dim * esize
+    return {"value": byts / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"heads 0..{heads - 1} of {w.name} (all keys), forward, fp64 numpy/BLAS; "
+                      f"{dt:.1f} s for {byts / 1e9:.2f} GB of inputs"}
+
+
 def gemm_reference(n: int = 16384, reps: int = 10) -> float:
     """Dense bf16 GEMM throughput of the platform library (torch.mm, which
     calls hipBLASLt) on this GPU, TFLOP/s: a measured reference for what the
@@ -492,7 +566,7 @@ def main():
                          "single-setting passes with the library's path choice")
     args = ap.parse_args()
     if args.pmc_summary:
-        pmc_summary(*args.pmc_summary)
+        pmc_summary(*args.pmc_summary, workload=args.workload)
         return
     if args.sq_summary:
         sq_summary(args.sq_summary)
@@ -523,6 +597,9 @@ def main():
     t_up = time.perf_counter()
     q1, k1, q2, k2 = upload(w, threads)
     t_up = time.perf_counter() - t_up
+    if w.n_q == 1:
+        decode_mode(w, args, (q1, k1, q2, k2), t_up)
+        return
     scale, causal = w.scale, w.causal
     E = w.elements()
     d = w.head_dim

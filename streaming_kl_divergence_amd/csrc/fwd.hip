@@ -303,20 +303,37 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   }
 }
 
-// Merge the partial states of all key ranges of each row and finish the row.
+// Merge the partial states of all key ranges of each row and finish the row
+// (the merge of the pages' Methodology 3, Split-K Variant).  One wave per row:
+// lane l takes ranges l, l + 64, ...; the maxima and then the rescaled sums
+// are reduced across the wave.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) v = fmaxf(v, __shfl_xor(v, x));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int x = 32; x >= 1; x >>= 1) v += __shfl_xor(v, x);
+  return v;
+}
+
 __global__ __launch_bounds__(256) void splitk_combine_kernel(FwdParams p) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);   // row; the same for the whole wave
   const int rows = p.heads * p.n_q;
   if (i >= rows) return;
   const float c = p.c;
   float M1 = kMaxInit, M2 = kMaxInit;
-  for (int s = 0; s < p.splits; ++s) {
+  for (int s = lane; s < p.splits; s += 64) {
     const float* st = p.part + ((size_t)s * rows + i) * 5;
     M1 = fmaxf(M1, st[0]);
     M2 = fmaxf(M2, st[3]);
   }
+  M1 = wave_max(M1);
+  M2 = wave_max(M2);
   float L1 = 0.f, L2 = 0.f, ACC = 0.f;
-  for (int s = 0; s < p.splits; ++s) {
+  for (int s = lane; s < p.splits; s += 64) {
     const float* st = p.part + ((size_t)s * rows + i) * 5;
     const float w1 = fast_exp2((st[0] - M1) * c);
     const float w2 = fast_exp2((st[3] - M2) * c);
@@ -324,11 +341,16 @@ __global__ __launch_bounds__(256) void splitk_combine_kernel(FwdParams p) {
     ACC = fmaf(st[2], w1, ACC);
     L2 = fmaf(st[4], w2, L2);
   }
-  const float lse1 = M1 * p.scale + log2f(L1) * kLn2;
-  const float lse2 = M2 * p.scale + log2f(L2) * kLn2;
-  p.kl[i] = p.scale * ACC / L1 + lse2 - lse1;
-  p.lse1[i] = lse1;
-  p.lse2[i] = lse2;
+  L1 = wave_sum(L1);
+  ACC = wave_sum(ACC);
+  L2 = wave_sum(L2);
+  if (lane == 0) {
+    const float lse1 = M1 * p.scale + log2f(L1) * kLn2;
+    const float lse2 = M2 * p.scale + log2f(L2) * kLn2;
+    p.kl[i] = p.scale * ACC / L1 + lse2 - lse1;
+    p.lse1[i] = lse1;
+    p.lse2[i] = lse2;
+  }
 }
 
 template <typename T, int D, int NW, bool SPLIT>
@@ -356,7 +378,7 @@ hipError_t launch_fwd(const FwdParams& p, int dtype, int head_dim, int nw, bool 
 
 hipError_t launch_splitk_combine(const FwdParams& p, hipStream_t stream) {
   const int rows = p.heads * p.n_q;
-  hipLaunchKernelGGL(splitk_combine_kernel, dim3((rows + 255) / 256), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(splitk_combine_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
