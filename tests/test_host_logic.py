@@ -107,6 +107,25 @@ def test_pmc_summary_scales_by_the_copy(tmp_path, monkeypatch):
     assert e["bytes_per_launch"] == 2300 * 1024 and e["source_hash"] == "abc"
 
 
+def test_traffic_files_per_workload(tmp_path, monkeypatch):
+    """Each workload's counter summary has its own file, and a summary is used
+    only while the device sources hash to what it was taken with."""
+    kv = "_ZN3skl13bwd_kv_kernelIDF16bLi128ELi1ELb0ELb0EEEvNS_9BwdParamsE"
+    gib_kib = (1 << 30) / 1024
+    _counter_csv(tmp_path / "f", [("__amd_rocclr_copyBuffer", "FETCH_SIZE", gib_kib), (kv, "FETCH_SIZE", 10.0)])
+    _counter_csv(tmp_path / "w", [("__amd_rocclr_copyBuffer", "WRITE_SIZE", gib_kib), (kv, "WRITE_SIZE", 0.0)])
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "h1")
+    bench.pmc_summary(str(tmp_path / "f"), str(tmp_path / "w"), workload="decode512k")
+    assert (tmp_path / "profiles" / "traffic_decode512k.json").exists()
+    assert not (tmp_path / "profiles" / "traffic.json").exists()
+    assert bench.measured_traffic("bwd_kv_kernel set1", "decode512k") == 10 * 1024
+    assert bench.measured_traffic("bwd_kv_kernel set1") is None
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "h2")
+    assert bench.measured_traffic("bwd_kv_kernel set1", "decode512k") is None
+
+
 def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
