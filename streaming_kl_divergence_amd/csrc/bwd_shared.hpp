@@ -59,22 +59,6 @@ __device__ __forceinline__ PackedDS pack_ds(const float* v) {
   return r;
 }
 
-// kgroup_mfma_tr with dS already packed.
-template <int D>
-__device__ __forceinline__ f32x16 kgroup_mfma_tr_packed(const SKL_LDS char* tile, int rbase, int db, const int* tb,
-                                                        const PackedDS& ds, f32x16 acc) {
-  constexpr int RB = D * 2;
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const SKL_LDS char* rows = tile + (rbase + 16 * t) * RB;
-    const u32x2 lo = read_tr4_at(rows + (tb[0] ^ (64 * db)));
-    const u32x2 hi = read_tr4_at(rows + (tb[1] ^ (64 * db)));
-    const u32x4 a = u32x4{lo.x, lo.y, hi.x, hi.y};
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), ds.b[t], acc, 0, 0, 0);
-  }
-  return acc;
-}
-
 // Fill n floats with zeros (n a multiple of 4, p 16-byte aligned); a kernel,
 // not hipMemsetAsync, so the call can sit in a captured graph.
 hipError_t zero_fill(float* p, size_t n, hipStream_t s);
