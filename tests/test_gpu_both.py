@@ -4,6 +4,7 @@ import numpy as np
 import pytest
 
 import oracle
+import workloads as W
 from tests.gpu_util import device_inputs, log, need_gpu
 from tests.parity import bf16_ds_bound, compare
 from tests.test_gpu_backward import BWD_EDGE
@@ -70,3 +71,25 @@ def test_rejects_missing_kl():
     kl, l1, l2 = skl.fwd(*dev, 0.125, False)
     with pytest.raises(ValueError):
         skl.bwd_both(*dev, 0.125, False, l1, l2, None)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_teacher_and_student_give_exact_zeros(causal):
+    """(Q1, K1) = (Q2, K2): P1 and P2 come out of the same arithmetic, so
+    dS2 = P2 - P1 and dS1 = P1 (r - KL) vanish exactly and all four gradients
+    of the both-settings kernels are zero (bitwise), with and without g."""
+    need_gpu()
+    import torch
+    import streaming_kl_divergence_amd as skl
+    log(f"case both identical inputs causal={causal}")
+    rng = np.random.default_rng(78)
+    q = W.round_bf16(rng.standard_normal((2, 300, 128), dtype=np.float32))
+    k = W.round_bf16(rng.standard_normal((2, 500, 128), dtype=np.float32))
+    dev = device_inputs([q, k, q, k], "bf16")
+    kl, l1, l2 = skl.fwd(*dev, 0.09, causal)
+    g = torch.from_numpy(rng.uniform(0.5, 1.5, (2, 300)).astype(np.float32)).cuda()
+    for dkl in (None, g):
+        out = skl.bwd_both(*dev, 0.09, causal, l1, l2, kl, dkl=dkl)
+        torch.cuda.synchronize()
+        for name, t in zip(("dq1", "dk1", "dq2", "dk2"), out):
+            assert not bool(t.any()), f"{name} nonzero (g={'given' if dkl is not None else 'ones'})"
