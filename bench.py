@@ -438,6 +438,14 @@ def sweep_mode(which: str):
                                                           **kw), stream, 1, reps))
                     row[f"bwd_set{st}_ms"] = round(float(ms), 3)
                     row[f"bwd_set{st}_tflops"] = round(8 * d * E / (ms * 1e-3) / 1e12, 1)
+                # both settings from one recomputation (bf16 kernels)
+                dq2 = torch.empty(H, n, d, device="cuda")
+                dk2 = torch.empty(H, n, d, device="cuda")
+                ms = np.median(_timed(lambda: skl.bwd_both(q1, k1, q2, k2, scale, causal, l1, l2, kl, dq1=dq, dk1=dk,
+                                                           dq2=dq2, dk2=dk2), stream, 1, reps))
+                row["bwd_both_ms"] = round(float(ms), 3)
+                row["bwd_both_tflops"] = round(16 * d * E / (ms * 1e-3) / 1e12, 1)
+                del dq2, dk2
                 emit(**row)
                 del q1, k1, q2, k2, dq, dk, kl, l1, l2
                 torch.cuda.empty_cache()
