@@ -35,6 +35,10 @@ Usage:
   python bench.py --copy-calibration ...
       also runs one plain 1 GiB device copy first, so that a rocprofv3 --pmc
       run sees FETCH_SIZE / WRITE_SIZE of a copy of known size.
+  python bench.py --calibrate
+      the calibration probes (libstreamkl_probes.so): a pure bf16 MFMA loop,
+      the v_exp_f32 issue rate, a plain 8 GiB HBM read and fp32 atomic adds,
+      the measured ceilings beside the published peaks.
   python bench.py --workload decode512k
       the decode line instead: the split-K forward for one query per head,
       rated in GB/s against the HBM peak.
@@ -453,6 +457,64 @@ def sweep_mode(which: str):
         raise SystemExit(f"unknown sweep {which!r}")
 
 
+def calibrate_mode(reps: int = 5):
+    """The calibration probes (libstreamkl_probes.so): a pure bf16 MFMA loop,
+    a v_exp_f32 stream, a plain 8 GiB read and fp32 atomic adds into a 1 GiB
+    and a 2 MiB buffer.  One JSON line; rates are medians of `reps` timed runs.
+    Cycle figures assume the nominal 2.4 GHz shader clock."""
+    import torch
+    from streaming_kl_divergence_amd import _lib
+    P = _lib.probes()
+    T = P.streamkl_probe_threads()
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    clk = 2.4e9
+
+    def run(launch):
+        def f():
+            if launch() != 0:
+                raise RuntimeError("probe launch failed")
+        return float(np.median(_timed(f, stream, 2, reps)))
+
+    out = {"probe": "calibration", "compute_units": cus, "nominal_clock_ghz": clk / 1e9}
+    # matrix cores: 16 waves per CU (4 per SIMD), 4 MFMAs of 32768 flop per trip
+    wg, iters = 4 * cus, 20000
+    sink = torch.empty(wg * T, device="cuda")
+    ms = run(lambda: P.streamkl_probe_mfma(wg, iters, sink.data_ptr(), sink.numel(), s))
+    tf = wg * 4 * iters * 4 * 32768 / (ms * 1e-3) / 1e12
+    out["mfma_bf16_tflops"] = round(tf, 1)
+    out["mfma_bf16_frac_of_peak"] = round(tf / PEAK_BF16_TFLOPS, 4)
+    # v_exp_f32: 8 per lane per trip, 16 waves per CU
+    iters = 20000
+    ms = run(lambda: P.streamkl_probe_exp(wg, iters, sink.data_ptr(), sink.numel(), s))
+    wave_insts = wg * 4 * iters * 8
+    out["exp_wave_insts_per_s"] = wave_insts / (ms * 1e-3)
+    out["exp_cycles_per_wave_inst_per_simd"] = round(4 * cus * clk * (ms * 1e-3) / wave_insts, 2)
+    del sink
+    # HBM read: 8 GiB, 8 workgroups per CU
+    nbytes = 8 << 30
+    src = torch.empty(nbytes // 4, device="cuda", dtype=torch.float32).fill_(1.0)
+    best = 0.0
+    for wgr in (4 * cus, 8 * cus, 16 * cus, 32 * cus):
+        snk = torch.empty(wgr * T, device="cuda", dtype=torch.int32)
+        ms = run(lambda: P.streamkl_probe_read(src.data_ptr(), nbytes, wgr, snk.data_ptr(), snk.numel() * 4, s))
+        out[f"read_gbs_{wgr}wg"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+        best = max(best, nbytes / (ms * 1e-3) / 1e9)
+        del snk
+    out["read_gbs_best"] = round(best, 1)
+    out["read_frac_of_hbm_peak"] = round(best / PEAK_HBM_GBS, 4)
+    del src
+    # fp32 atomics: 1 GiB (the size of one 64K-causal dQ) and 2 MiB (fits one XCD's L2)
+    for name, n, r in (("1GiB", (1 << 30) // 4, 2), ("2MiB", (2 << 20) // 4, 512)):
+        dst = torch.zeros(n, device="cuda", dtype=torch.float32)
+        ms = run(lambda: P.streamkl_probe_atomic(dst.data_ptr(), n, 8 * cus, r, s))
+        out[f"atomic_f32_payload_gbs_{name}"] = round(4 * n * r / (ms * 1e-3) / 1e9, 1)
+        del dst
+    torch.cuda.empty_cache()
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline():
     """The fp64 oracle, as it stands, on a bounded sample of the same workload:
     head 0 of the 64K causal workload restricted to its first 16384 queries and
@@ -474,7 +536,8 @@ def cpu_baseline():
     oracle.backward_head(2, q1, k1, q2, k2, w.scale, True)
     dt = time.perf_counter() - t0
     flop = 20 * w.head_dim * sub.elements()
-    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "host_cores": os.cpu_count(),
+            "kind": "oracle",
             "sample": f"head 0 of causal64k, first {n} queries x {n} keys (causal), fwd + bwd Setting 1 + "
                       f"Setting 2, fp64 numpy/BLAS; {dt:.1f} s for {flop / 1e12:.3f} TFLOP"}
 
@@ -538,7 +601,8 @@ def cpu_baseline_decode(w: W.Workload, heads: int = 0):
             dt += time.perf_counter() - t0
     esize = 2 if w.dtype == "bf16" else 4
     byts = heads * 2 * (w.n_k + w.n_q) * w.head_dim * esize
-    return {"value": byts / dt / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+    return {"value": byts / dt / 1e9, "unit": "GB/s", "cores": cores, "host_cores": os.cpu_count(),
+            "kind": "oracle",
             "sample": f"heads 0..{heads - 1} of {w.name} (all keys), forward, fp64 numpy/BLAS; "
                       f"{dt:.1f} s for {byts / 1e9:.2f} GB of inputs"}
 
@@ -567,6 +631,8 @@ def main():
     ap.add_argument("--configs", action="store_true")
     ap.add_argument("--sweep", choices=("crossover", "splitk", "context"))
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="run the calibration probes (MFMA loop, v_exp_f32, HBM read, fp32 atomics)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--sq-summary", nargs="+", metavar="DIR")
     ap.add_argument("--bwd-path", choices=("both", "separate"), default="both",
@@ -594,6 +660,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.calibrate:
+        calibrate_mode()
+        return
     if args.configs:
         configs_mode()
         return
@@ -698,7 +767,6 @@ def main():
     if not args.no_gemm_ref:
         gemm = gemm_reference()
         parts["gemm_bf16_16384_tflops"] = round(gemm, 1)
-        parts["pct_of_gemm_step"] = round(100 * value / gemm, 1)
     parts["wall_s_timed"] = round(wall, 3)
     parts["upload_s"] = round(t_up, 1)
 

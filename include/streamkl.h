@@ -115,8 +115,9 @@ int streamkl_fwd_splitk(const void* q1, const void* k1, const void* q2, const vo
  * head_dim]), overwriting them.  lse1, lse2 are the forward's outputs for the
  * same inputs.  `path` picks the fused or separate kernels (AUTO: the
  * library's choice); DK_ONLY / DQ_ONLY compute one of the two gradients.
- * Calling DK_ONLY then DQ_ONLY gives the same result as SEPARATE.  workspace: at least streamkl_workspace_bytes(1, ...)
- * bytes (may be NULL when that is 0).
+ * Calling DK_ONLY then DQ_ONLY gives the same result as SEPARATE.
+ * workspace: at least streamkl_workspace_bytes(1, ...) bytes (may be NULL
+ * when that is 0, which it is for every shape today).
  */
 int streamkl_bwd_set1(const void* q1, const void* k1, const void* q2, const void* k2,
                       int n_q, int n_k, int heads, int head_dim, int causal, float scale,
@@ -171,10 +172,14 @@ size_t streamkl_workspace_bytes(int op, int n_q, int n_k, int heads, int head_di
 int streamkl_splitk_auto(int n_q, int n_k, int heads, int head_dim);
 
 /* The backward path AUTO resolves to for this shape (STREAMKL_BWD_FUSED or
- * STREAMKL_BWD_SEPARATE).  The pages (Methodology 3, Kernel Fusion) prefer the
- * fused kernel while the dQ buffer fits the cache; on MI355X its fp32 atomics
- * made it slower than the separate kernels at every measured size, so this
- * returns STREAMKL_BWD_SEPARATE for every shape. */
+ * STREAMKL_BWD_SEPARATE).  The pages (Methodology 2, Recomputation Strategy,
+ * its Kernel Fusion paragraph) prefer the fused kernel while the dQ buffer
+ * fits the cache.  On MI355X the fused kernel moves 4 * head_dim / 128 bytes of
+ * fp32 atomics per (query, key) pair and was measured slower than the separate
+ * kernels at every size tried (64 to 16K queries against 128K keys, both
+ * settings), so the result does not depend on the arguments: it is
+ * STREAMKL_BWD_SEPARATE for every shape.  The arguments are kept so that a
+ * shape-dependent rule can be added without changing the ABI. */
 int streamkl_bwd_select(int n_q, int n_k, int heads, int head_dim, int causal);
 
 /* Static text for a status code. */

@@ -1,0 +1,52 @@
+/*
+ * streamkl_probes.h - calibration probes for MI355X (gfx950), in their own
+ * library (libstreamkl_probes.so) beside the attention-KL library.
+ *
+ * Each probe is one kernel with an exactly known amount of work; the caller
+ * times it on `stream` with HIP events and divides.  They measure what the
+ * hardware delivers to simple code on this GPU, the ceilings that the
+ * attention-KL kernels are compared with:
+ *   streamkl_probe_mfma    bf16 matrix-core rate (v_mfma_f32_32x32x16_bf16,
+ *                          32768 flop per wave instruction, 4 per loop trip);
+ *   streamkl_probe_exp     v_exp_f32 issue rate (8 per lane per loop trip);
+ *   streamkl_probe_read    HBM read rate (16-byte loads, grid-stride);
+ *   streamkl_probe_atomic  fp32 atomic-add rate (4-byte payload per add).
+ * They compute nothing of the method itself.
+ *
+ * Pointers are caller-owned device memory; nothing is allocated.  Returns 0,
+ * -1 for invalid arguments (nothing launched) or -6 for a launch error.
+ */
+#ifndef STREAMKL_PROBES_H
+#define STREAMKL_PROBES_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Threads per workgroup of every probe (sink arrays hold one value per thread). */
+int streamkl_probe_threads(void);
+
+/* workgroups x 4 waves, each `iters` trips of 4 independent MFMAs on register
+ * operands.  sink: >= workgroups * threads floats (written, meaningless). */
+int streamkl_probe_mfma(int workgroups, int iters, float* sink, size_t sink_floats, hipStream_t stream);
+
+/* workgroups x 256 threads, each `iters` trips of 8 independent v_exp_f32.
+ * sink: >= workgroups * threads floats. */
+int streamkl_probe_exp(int workgroups, int iters, float* sink, size_t sink_floats, hipStream_t stream);
+
+/* Reads `bytes` (a multiple of 16) of src (16-byte aligned) once.
+ * sink: >= workgroups * threads * 4 bytes. */
+int streamkl_probe_read(const void* src, size_t bytes, int workgroups, void* sink, size_t sink_bytes,
+                        hipStream_t stream);
+
+/* Adds 1.0f to each of dst[0 .. n_floats) `reps` times with fp32 atomics. */
+int streamkl_probe_atomic(float* dst, size_t n_floats, int workgroups, int reps, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STREAMKL_PROBES_H */

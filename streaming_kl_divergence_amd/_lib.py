@@ -13,7 +13,8 @@ ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_SCALE, ERR_WORKSPACE, ERR_HIP, ERR_ALI
 BF16, FP32 = 0, 1
 BWD_AUTO, BWD_FUSED, BWD_SEPARATE, BWD_DK_ONLY, BWD_DQ_ONLY = 0, 1, 2, 3, 4
 
-EXPORTS = ("streamkl_fwd", "streamkl_fwd_splitk", "streamkl_bwd_set1", "streamkl_bwd_set2", "streamkl_bwd_both",
+EXPORTS = ("streamkl_fwd", "streamkl_fwd_splitk", "streamkl_bwd_set1",
+           "streamkl_bwd_set2", "streamkl_bwd_both",
            "streamkl_workspace_bytes", "streamkl_splitk_auto", "streamkl_bwd_select", "streamkl_strerror")
 
 _P = ctypes.c_void_p
@@ -35,6 +36,33 @@ _SIGS = {
 }
 
 _lib = None
+
+PROBES_PATH = os.path.join(PKG, "libstreamkl_probes.so")
+PROBE_EXPORTS = ("streamkl_probe_threads", "streamkl_probe_mfma", "streamkl_probe_exp", "streamkl_probe_read",
+                 "streamkl_probe_atomic")
+_PROBE_SIGS = {
+    "streamkl_probe_threads": (_I, []),
+    "streamkl_probe_mfma": (_I, [_I, _I, _P, _Z, _P]),
+    "streamkl_probe_exp": (_I, [_I, _I, _P, _Z, _P]),
+    "streamkl_probe_read": (_I, [_P, _Z, _I, _P, _Z, _P]),
+    "streamkl_probe_atomic": (_I, [_P, _Z, _I, _I, _P]),
+}
+_probes = None
+
+
+def probes() -> ctypes.CDLL:
+    """Load libstreamkl_probes.so (calibration kernels; bench.py --calibrate)."""
+    global _probes
+    if _probes is None:
+        if not os.path.exists(PROBES_PATH):
+            raise ImportError(f"{PROBES_PATH} is not built; run `python -m streaming_kl_divergence_amd.build`")
+        l = ctypes.CDLL(PROBES_PATH)
+        for name, (res, args) in _PROBE_SIGS.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _probes = l
+    return _probes
 
 
 class StreamKLError(RuntimeError):

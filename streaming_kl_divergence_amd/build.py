@@ -20,6 +20,9 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libstreamkl.so")
 SOURCES = ["fwd.hip", "bwd.hip", "bwd_both.hip", "api.cpp"]
+# calibration probes (bench.py --calibrate), a library of their own
+PROBES_LIB = os.path.join(PKG, "libstreamkl_probes.so")
+PROBES_SOURCES = ["probes.hip"]
 ARCH = "gfx950"
 
 
@@ -58,18 +61,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs: list[str], out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBES_SOURCES
+    with ThreadPoolExecutor(len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBES_SOURCES], PROBES_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBES_LIB}")
     return LIB
 
 

@@ -82,6 +82,27 @@ int effective_splits(int n_k, int splits) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? STREAMKL_OK : STREAMKL_ERR_HIP; }
 
+// Split count of a validated split-K call, and the partial-state bytes it needs.
+int splitk_count(int n_q, int n_k, int heads, int head_dim, int num_splits, size_t* need) {
+  const int splits = num_splits == 0 ? streamkl_splitk_auto(n_q, n_k, heads, head_dim)
+                                     : effective_splits(n_k, num_splits);
+  *need = (size_t)splits * heads * n_q * 5 * sizeof(float);
+  return splits;
+}
+
+// The partial kernel, then the combine, on `stream`, with the partial states in `part`.
+int splitk_launch(const void* q1, const void* k1, const void* q2, const void* k2, int n_q, int n_k, int heads,
+                  int head_dim, int causal, float scale, streamkl_dtype dtype, int splits, float* kl, float* lse1,
+                  float* lse2, float* part, hipStream_t stream) {
+  skl::FwdParams p = fwd_params(q1, k1, q2, k2, n_q, n_k, heads, causal, scale, kl, lse1, lse2);
+  p.part = part;
+  p.splits = splits;
+  p.split_keys = split_keys_for(n_k, splits);
+  hipError_t e = skl::launch_fwd(p, (int)dtype, head_dim, skl::fwd_waves(n_q), true, stream);
+  if (e != hipSuccess) return STREAMKL_ERR_HIP;
+  return status_of(skl::launch_splitk_combine(p, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -107,9 +128,9 @@ size_t streamkl_workspace_bytes(int op, int n_q, int n_k, int heads, int head_di
   if (n_q < 1 || n_k < 1 || heads < 1 || (head_dim != 64 && head_dim != 128)) return (size_t)-1;
   if (op == 0) {
     if (num_splits < 0 || num_splits > kMaxSplits) return (size_t)-1;
-    const int s = num_splits == 0 ? streamkl_splitk_auto(n_q, n_k, heads, head_dim)
-                                  : effective_splits(n_k, num_splits);
-    return (size_t)s * heads * n_q * 5 * sizeof(float);
+    size_t need = 0;
+    splitk_count(n_q, n_k, heads, head_dim, num_splits, &need);
+    return need;
   }
   if (op == 1 || op == 2) {
     if ((int)path < STREAMKL_BWD_AUTO || (int)path > STREAMKL_BWD_DQ_ONLY) return (size_t)-1;
@@ -136,18 +157,12 @@ int streamkl_fwd_splitk(const void* q1, const void* k1, const void* q2, const vo
   if (st) return st;
   if (!kl || !lse1 || !lse2) return STREAMKL_ERR_NULL;
   if (num_splits < 0 || num_splits > kMaxSplits) return STREAMKL_ERR_UNSUPPORTED;
-  const int splits = num_splits == 0 ? streamkl_splitk_auto(n_q, n_k, heads, head_dim)
-                                     : effective_splits(n_k, num_splits);
-  const size_t need = (size_t)splits * heads * n_q * 5 * sizeof(float);
+  size_t need = 0;
+  const int splits = splitk_count(n_q, n_k, heads, head_dim, num_splits, &need);
   if (!workspace || workspace_bytes < need) return STREAMKL_ERR_WORKSPACE;
   if (!aligned16(workspace)) return STREAMKL_ERR_ALIGN;
-  skl::FwdParams p = fwd_params(q1, k1, q2, k2, n_q, n_k, heads, causal, scale, kl, lse1, lse2);
-  p.part = (float*)workspace;
-  p.splits = splits;
-  p.split_keys = split_keys_for(n_k, splits);
-  hipError_t e = skl::launch_fwd(p, (int)dtype, head_dim, skl::fwd_waves(n_q), true, stream);
-  if (e != hipSuccess) return STREAMKL_ERR_HIP;
-  return status_of(skl::launch_splitk_combine(p, stream));
+  return splitk_launch(q1, k1, q2, k2, n_q, n_k, heads, head_dim, causal, scale, dtype, splits, kl, lse1, lse2,
+                       (float*)workspace, stream);
 }
 
 int streamkl_bwd_select(int n_q, int n_k, int heads, int head_dim, int causal) {
@@ -156,13 +171,14 @@ int streamkl_bwd_select(int n_q, int n_k, int heads, int head_dim, int causal) {
   (void)heads;
   (void)head_dim;
   (void)causal;
-  // The pages' rule (Methodology 3, Kernel Fusion) takes the fused kernel while
-  // dQ fits the cache.  On MI355X the fused kernel moves 4*d/128 bytes of fp32
-  // atomics per (query, key) pair, about six times the time of the score
-  // recomputation it saves, and measured slower than the separate kernels at
-  // every size tried: 0.94x at 64 queries x 128K keys (dQ 1 MiB) down to
-  // 0.44x at 16K queries, both settings.  So AUTO takes the separate kernels;
-  // the fused path stays available on request.
+  // The pages' rule (Methodology 2, Recomputation Strategy, Kernel Fusion
+  // paragraph) takes the fused kernel while dQ fits the cache.  On MI355X the
+  // fused kernel moves 4*d/128 bytes of fp32 atomics per (query, key) pair,
+  // about six times the time of the score recomputation it saves, and
+  // measured slower than the separate kernels at every size tried: 0.94x at
+  // 64 queries x 128K keys (dQ 1 MiB) down to 0.44x at 16K queries, both
+  // settings.  So AUTO takes the separate kernels whatever the shape; the
+  // fused path stays available on request.
   return STREAMKL_BWD_SEPARATE;
 }
 

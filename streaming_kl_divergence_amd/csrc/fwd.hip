@@ -117,12 +117,16 @@ __device__ __forceinline__ void tile_update(RowState& st, f32x16* s1, f32x16* s2
 // tile's maxima.  The sums are scale-free, so any offset gives the same
 // result as long as no term overflows: the fold is accepted when every lane's
 // tile sum of 2^(x c - m c) stays below 2^64 (no score more than ~64 binary
-// orders above its offset), and otherwise the whole wave raises its offsets
-// to the tile maxima (rescaling l and acc, exactly the online update of the
-// pages' Methodology 1) and folds again, which cannot overflow.  An offset
-// never exceeds the true running maximum, so nothing underflows that the
-// exact update would keep.  The first tile of a lane always takes the raise
-// (its offset is the initial -1e30).  Saves the per-tile max reduction.
+// orders above its offset).  Otherwise nothing is changed and the caller runs
+// the exact online update of the pages' Methodology 1 on the tile
+// (tile_update: offsets raised to the tile maxima, l and acc rescaled), lane
+// by lane, which cannot overflow.  An offset never exceeds the true running
+// maximum, so nothing underflows that the exact update would keep.  The
+// first tile of a lane always takes the exact update (its offset is the
+// initial -1e30).  Saves the per-tile max reduction.  A lane whose scores
+// are not finite (NaN or infinite inputs) also fails the test; the exact
+// update then makes that lane's row non-finite and leaves every other lane's
+// row exact.
 template <int NKB>
 __device__ __forceinline__ bool tile_fold_at_offsets(RowState& st, const f32x16* s1, const f32x16* s2, float c) {
   const float mc1 = st.m1 * c, mc2 = st.m2 * c;
@@ -146,25 +150,6 @@ __device__ __forceinline__ bool tile_fold_at_offsets(RowState& st, const f32x16*
   st.l2 += t2;
   st.acc += (sa[0] + sa[1]) + (sa[2] + sa[3]);
   return true;
-}
-
-template <int NKB>
-__device__ __forceinline__ void raise_offsets(RowState& st, const f32x16* s1, const f32x16* s2, float c) {
-  float tm1 = -INFINITY, tm2 = -INFINITY;
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      tm1 = fmaxf(tm1, s1[kb][r]);
-      tm2 = fmaxf(tm2, s2[kb][r]);
-    }
-  const float n1 = fmaxf(st.m1, tm1), n2 = fmaxf(st.m2, tm2);
-  const float a1 = fast_exp2((st.m1 - n1) * c), a2 = fast_exp2((st.m2 - n2) * c);
-  st.m1 = n1;
-  st.m2 = n2;
-  st.l1 *= a1;
-  st.acc *= a1;
-  st.l2 *= a2;
 }
 
 template <typename T, int D, int NW, bool SPLIT>
@@ -271,8 +256,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
     if (need_mask) {
       tile_update<true, NKB>(st, s1, s2, c, k0, h, klimit, p.causal, qlim);
     } else if (!tile_fold_at_offsets<NKB>(st, s1, s2, c)) {
-      raise_offsets<NKB>(st, s1, s2, c);
-      tile_fold_at_offsets<NKB>(st, s1, s2, c);
+      tile_update<false, NKB>(st, s1, s2, c, k0, h, klimit, p.causal, qlim);
     }
   }
 

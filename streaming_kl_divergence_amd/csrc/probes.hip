@@ -1,0 +1,127 @@
+// Calibration probes for the ceilings quoted beside the attention-KL kernels:
+// how fast this GPU runs a pure bf16 MFMA loop, a stream of v_exp_f32, a
+// plain read of a large buffer and fp32 atomic adds.  Each probe is one
+// kernel whose work is known exactly; the caller times it with HIP events.
+// Every access stays inside the buffers the caller passes (sizes checked on
+// the host), and every loop has a fixed trip count.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "streamkl_probes.h"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+
+// Four independent accumulator chains of v_mfma_f32_32x32x16_bf16 per wave,
+// operands in registers.  One lane's sum of the results goes to sink[gid] so
+// that nothing is optimised away.
+__global__ __launch_bounds__(kThreads) void mfma_loop(int iters, float* __restrict__ sink) {
+  const int gid = blockIdx.x * kThreads + threadIdx.x;
+  bf16x8 a, b;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    a[e] = (__bf16)(0.001f * (float)((threadIdx.x + e) & 7));
+    b[e] = (__bf16)(0.002f * (float)((threadIdx.x * 3 + e) & 7));
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, b, c3, 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  sink[gid] = s;
+}
+
+// Eight independent chains x <- 2^(-x) of v_exp_f32 per lane (the negation is
+// a free source modifier), so the loop is one transcendental instruction per
+// element and its rate is the issue rate of v_exp_f32.
+__global__ __launch_bounds__(kThreads) void exp_loop(int iters, float* __restrict__ sink) {
+  const int gid = blockIdx.x * kThreads + threadIdx.x;
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = 0.01f * (float)((threadIdx.x + j) & 15);
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = __builtin_amdgcn_exp2f(-x[j]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += x[j];
+  sink[gid] = s;
+}
+
+// Grid-stride read of n16 16-byte words, four independent loads in flight
+// per thread; a per-thread XOR of what was read goes to sink[gid].
+__global__ __launch_bounds__(kThreads) void read_loop(const uint4* __restrict__ src, size_t n16,
+                                                       uint32_t* __restrict__ sink) {
+  const size_t gid = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * kThreads;
+  uint32_t acc = 0;
+  size_t i = gid;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
+    acc ^= (v0.x ^ v0.y ^ v0.z ^ v0.w) ^ (v1.x ^ v1.y ^ v1.z ^ v1.w) ^ (v2.x ^ v2.y ^ v2.z ^ v2.w) ^
+           (v3.x ^ v3.y ^ v3.z ^ v3.w);
+  }
+  for (; i < n16; i += stride) {
+    const uint4 v = src[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  sink[gid] = acc;
+}
+
+// `reps` passes of one fp32 atomic add of 1.0 to each of the n floats of dst,
+// consecutive lanes on consecutive addresses.
+__global__ __launch_bounds__(kThreads) void atomic_loop(float* __restrict__ dst, size_t n, int reps) {
+  const size_t gid = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  const size_t stride = (size_t)gridDim.x * kThreads;
+  for (int r = 0; r < reps; ++r)
+    for (size_t i = gid; i < n; i += stride) atomicAdd(dst + i, 1.0f);
+}
+
+int status(hipError_t e) { return e == hipSuccess ? 0 : -6; }
+
+}  // namespace
+
+extern "C" {
+
+int streamkl_probe_threads(void) { return kThreads; }
+
+int streamkl_probe_mfma(int workgroups, int iters, float* sink, size_t sink_floats, hipStream_t stream) {
+  if (workgroups < 1 || iters < 1 || !sink || sink_floats < (size_t)workgroups * kThreads) return -1;
+  hipLaunchKernelGGL(mfma_loop, dim3(workgroups), dim3(kThreads), 0, stream, iters, sink);
+  return status(hipGetLastError());
+}
+
+int streamkl_probe_exp(int workgroups, int iters, float* sink, size_t sink_floats, hipStream_t stream) {
+  if (workgroups < 1 || iters < 1 || !sink || sink_floats < (size_t)workgroups * kThreads) return -1;
+  hipLaunchKernelGGL(exp_loop, dim3(workgroups), dim3(kThreads), 0, stream, iters, sink);
+  return status(hipGetLastError());
+}
+
+int streamkl_probe_read(const void* src, size_t bytes, int workgroups, void* sink, size_t sink_bytes,
+                        hipStream_t stream) {
+  if (!src || !sink || workgroups < 1 || bytes % 16 != 0 || ((uintptr_t)src & 15) != 0 ||
+      sink_bytes < (size_t)workgroups * kThreads * sizeof(uint32_t))
+    return -1;
+  hipLaunchKernelGGL(read_loop, dim3(workgroups), dim3(kThreads), 0, stream, (const uint4*)src, bytes / 16,
+                     (uint32_t*)sink);
+  return status(hipGetLastError());
+}
+
+int streamkl_probe_atomic(float* dst, size_t n_floats, int workgroups, int reps, hipStream_t stream) {
+  if (!dst || n_floats < 1 || workgroups < 1 || reps < 1) return -1;
+  hipLaunchKernelGGL(atomic_loop, dim3(workgroups), dim3(kThreads), 0, stream, dst, n_floats, reps);
+  return status(hipGetLastError());
+}
+
+}  // extern "C"

@@ -29,6 +29,44 @@ def _inputs(q1, k1, q2, k2):
     return heads, n_q, n_k, d, _DT[q1.dtype]
 
 
+def check_rows(t, name: str, heads: int, n_q: int, device) -> None:
+    """A per-row array (lse1, lse2, kl, dkl): fp32 [heads, n_q], contiguous, on `device`."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}; the inputs are on {device}")
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != (heads, n_q):
+        raise ValueError(f"{name} must be a contiguous fp32 [{heads}, {n_q}] tensor")
+
+
+def check_out(t, name: str, shape, device) -> None:
+    """A caller-given gradient output: fp32 of `shape`, contiguous, on `device`."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}; the inputs are on {device}")
+    if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be a contiguous fp32 {list(shape)} tensor")
+
+
+def check_disjoint(named) -> None:
+    """Output tensors must not share memory (the kernels write them concurrently)."""
+    spans = []
+    for name, t in named:
+        if t is None:
+            continue
+        lo = t.data_ptr()
+        spans.append((lo, lo + t.numel() * t.element_size(), name))
+    spans.sort()
+    for (a0, a1, an), (b0, b1, bn) in zip(spans, spans[1:]):
+        if b0 < a1:
+            raise ValueError(f"outputs {an} and {bn} overlap")
+
+
 def _stream():
     return torch.cuda.current_stream().cuda_stream
 
@@ -57,6 +95,8 @@ def fwd_splitk(q1, k1, q2, k2, scale: float, causal: bool, num_splits: int = 0, 
     need = splitk_workspace_bytes(n_q, n_k, heads, d, num_splits)
     if workspace is None:
         workspace = torch.empty(max(need, 16), device=q1.device, dtype=torch.uint8)
+    elif workspace.device != q1.device or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {q1.device}")
     out = [torch.empty(heads, n_q, device=q1.device, dtype=torch.float32) for _ in range(3)]
     st = _lib.lib().streamkl_fwd_splitk(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), n_q, n_k,
                                         heads, d, int(causal), float(scale), dt, int(num_splits),
@@ -84,13 +124,17 @@ def bwd(setting: int, q1, k1, q2, k2, scale: float, causal: bool, lse1, lse2, kl
     heads, n_q, n_k, d, dt = _inputs(q1, k1, q2, k2)
     if path not in _PATH:
         raise ValueError(f"unknown path {path!r}")
+    if lse1 is None or lse2 is None:
+        raise ValueError("the backward needs the forward's lse1 and lse2")
+    for t, name in ((lse1, "lse1"), (lse2, "lse2"), (kl, "kl"), (dkl, "dkl")):
+        check_rows(t, name, heads, n_q, q1.device)
+    check_out(dq, "dq", (heads, n_q, d), q1.device)
+    check_out(dk, "dk", (heads, n_k, d), q1.device)
     if path != "dk_only" and dq is None:
         dq = torch.empty(heads, n_q, d, device=q1.device, dtype=torch.float32)
     if path != "dq_only" and dk is None:
         dk = torch.empty(heads, n_k, d, device=q1.device, dtype=torch.float32)
-    for t in (lse1, lse2, kl, dkl):
-        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or t.shape != (heads, n_q)):
-            raise ValueError("lse1, lse2, kl, dkl must be contiguous fp32 [heads, n_q]")
+    check_disjoint((("dq", dq if path != "dk_only" else None), ("dk", dk if path != "dq_only" else None)))
     L = _lib.lib()
     common = (q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), n_q, n_k, heads, d, int(causal),
               float(scale), dt, lse1.data_ptr(), lse2.data_ptr())
@@ -116,17 +160,18 @@ def bwd_both(q1, k1, q2, k2, scale: float, causal: bool, lse1, lse2, kl, dkl=Non
     heads, n_q, n_k, d, dt = _inputs(q1, k1, q2, k2)
     if path not in ("auto", "separate", "dk_only", "dq_only"):
         raise ValueError(f"unknown path {path!r}")
-    for t in (lse1, lse2, kl, dkl):
-        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous() or t.shape != (heads, n_q)):
-            raise ValueError("lse1, lse2, kl, dkl must be contiguous fp32 [heads, n_q]")
-    if kl is None:
-        raise ValueError("the both-settings backward needs the forward's KL rows")
+    if lse1 is None or lse2 is None or kl is None:
+        raise ValueError("the both-settings backward needs the forward's lse1, lse2 and KL rows")
+    for t, name in ((lse1, "lse1"), (lse2, "lse2"), (kl, "kl"), (dkl, "dkl")):
+        check_rows(t, name, heads, n_q, q1.device)
     outs = []
-    for o, n, want in ((dq1, n_q, path != "dk_only"), (dk1, n_k, path != "dq_only"),
-                       (dq2, n_q, path != "dk_only"), (dk2, n_k, path != "dq_only")):
+    for o, name, n, want in ((dq1, "dq1", n_q, path != "dk_only"), (dk1, "dk1", n_k, path != "dq_only"),
+                             (dq2, "dq2", n_q, path != "dk_only"), (dk2, "dk2", n_k, path != "dq_only")):
+        check_out(o, name, (heads, n, d), q1.device)
         if o is None and want:
             o = torch.empty(heads, n, d, device=q1.device, dtype=torch.float32)
         outs.append(o if want else None)
+    check_disjoint(zip(("dq1", "dk1", "dq2", "dk2"), outs))
     L = _lib.lib()
     st = L.streamkl_bwd_both(q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), n_q, n_k, heads, d,
                              int(causal), float(scale), dt, lse1.data_ptr(), lse2.data_ptr(), kl.data_ptr(),

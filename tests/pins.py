@@ -121,6 +121,16 @@ def pin_torch_autograd(oracle, seed=2):
             skl, sl1, sl2 = oracle.forward_head(q1, k1, q2, k2, scale, causal)
             dks = oracle.dk_keys_from_state(setting, q1, k1, q2, k2, scale, causal, keys, sl1, sl2, skl, g)
             assert np.allclose(dks, tdk[keys], rtol=1e-10, atol=1e-13), (setting, np.abs(dks - tdk[keys]).max())
+            # the logit gradient itself: contracted with the setting's keys and
+            # queries it must give torch's dQ and dK, and each of its rows sums
+            # to zero (Setting 1: sum P2 - sum P1 = 0; Setting 2: sum P1 r = KL)
+            ds = oracle.dlogits_head(setting, q1, k1, q2, k2, scale, causal, g)
+            q_t, k_t = (q2, k2) if setting == 1 else (q1, k1)
+            assert np.allclose(scale * ds @ k_t, tdq, rtol=1e-10, atol=1e-13), setting
+            assert np.allclose(scale * ds.T @ q_t, tdk, rtol=1e-10, atol=1e-13), setting
+            assert np.abs(ds.sum(1)).max() <= 1e-13 * max(1.0, np.abs(ds).max()), setting
+            mask = oracle.allowed_mask(np.arange(n_q), n_q, n_k, causal)
+            assert not np.any(ds[~mask]), setting
 
 
 # ---- P3: invariants ------------------------------------------------------------
@@ -288,5 +298,39 @@ def pin_streaming_identity(oracle, seed=6):
                 assert abs(got[1] - l1[i]) <= 1e-12 and abs(got[2] - l2[i]) <= 1e-12
 
 
+# ---- P2': the multi-head entry points against one batched library computation ----
+
+def pin_multihead(oracle, seed=7):
+    """oracle.forward / oracle.backward on [H, N, d] inputs against torch fp64
+    over the whole batch at once (batched matmul, log_softmax, kl_div and
+    autograd), with a different upstream weight per head and row."""
+    import torch
+    rng = np.random.default_rng(seed)
+    H, n_q, n_k, d = 3, 10, 14, 6
+    for causal in (False, True):
+        x = [rng.standard_normal((H, n, d)) for n in (n_q, n_k, n_q, n_k)]
+        g = 0.5 + rng.random((H, n_q))
+        scale = 0.55
+        kl, l1, l2 = oracle.forward(*x, scale, causal)
+        i = torch.arange(n_q)[:, None]
+        j = torch.arange(n_k)[None, :]
+        allowed = (j <= i + (n_k - n_q)) if causal else torch.ones(n_q, n_k, dtype=torch.bool)
+        for setting in (1, 2):
+            t = [torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in x]
+            s1 = (scale * torch.matmul(t[0], t[1].transpose(1, 2).contiguous())).masked_fill(~allowed, -1e30)
+            s2 = (scale * torch.matmul(t[2], t[3].transpose(1, 2).contiguous())).masked_fill(~allowed, -1e30)
+            assert np.allclose(l1, torch.logsumexp(s1, -1).detach().numpy(), rtol=1e-12, atol=1e-12)
+            assert np.allclose(l2, torch.logsumexp(s2, -1).detach().numpy(), rtol=1e-12, atol=1e-12)
+            lp1, lp2 = torch.log_softmax(s1, -1), torch.log_softmax(s2, -1)
+            lp1, lp2 = (lp1.detach(), lp2) if setting == 1 else (lp1, lp2.detach())
+            tkl = torch.nn.functional.kl_div(lp2, lp1, reduction="none", log_target=True).sum(-1)
+            assert np.allclose(kl, tkl.detach().numpy(), rtol=1e-11, atol=1e-13)
+            (torch.tensor(g) * tkl).sum().backward()
+            dq, dk = oracle.backward(setting, *x, scale, causal, g)
+            iq, ik = (2, 3) if setting == 1 else (0, 1)
+            assert np.allclose(dq, t[iq].grad.numpy(), rtol=1e-10, atol=1e-13), setting
+            assert np.allclose(dk, t[ik].grad.numpy(), rtol=1e-10, atol=1e-13), setting
+
+
 ALL_PINS = [pin_brute_force, pin_bernoulli, pin_torch_autograd, pin_invariants,
-            pin_uniform_teacher, pin_finite_differences, pin_streaming_identity]
+            pin_uniform_teacher, pin_finite_differences, pin_streaming_identity, pin_multihead]

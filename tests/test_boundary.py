@@ -10,12 +10,14 @@ import pytest
 
 from streaming_kl_divergence_amd import _lib as L
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "streamkl.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADER = os.path.join(INCLUDE, "streamkl.h")
+PROBES_HEADER = os.path.join(INCLUDE, "streamkl_probes.h")
 FAKE = 4096  # a non-NULL, 16-byte aligned address that is never dereferenced
 
 
-def declared_functions():
-    with open(HEADER) as f:
+def declared_functions(header=HEADER):
+    with open(header) as f:
         src = f.read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(streamkl_\w+)\s*\(", src)))
@@ -28,6 +30,22 @@ def test_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.EXPORTS)
+
+
+def test_probe_library_exports_and_validates():
+    lib = L.probes()
+    names = declared_functions(PROBES_HEADER)
+    assert set(names) == set(L.PROBE_EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    # invalid arguments are refused before any launch
+    t = lib.streamkl_probe_threads()
+    assert t == 256
+    assert lib.streamkl_probe_mfma(4, 10, FAKE, 4 * t - 1, None) == -1
+    assert lib.streamkl_probe_exp(0, 10, FAKE, 4 * t, None) == -1
+    assert lib.streamkl_probe_read(FAKE, 100, 4, FAKE, 4 * t * 4, None) == -1      # not a multiple of 16
+    assert lib.streamkl_probe_read(FAKE + 4, 64, 4, FAKE, 4 * t * 4, None) == -1   # misaligned
+    assert lib.streamkl_probe_atomic(None, 16, 4, 1, None) == -1
 
 
 def _fwd(**kw):
@@ -133,3 +151,39 @@ def test_missing_library_fails_loudly(monkeypatch):
     monkeypatch.setattr(L, "LIB_PATH", "/nonexistent/libstreamkl.so")
     with pytest.raises(ImportError):
         L.lib()
+
+
+def test_wrapper_rejects_bad_saved_state_and_outputs():
+    """The torch wrapper checks every tensor it hands to the library (device,
+    dtype, contiguity, shape, overlap) so that a host pointer or an undersized
+    buffer never reaches a kernel."""
+    import torch
+    from streaming_kl_divergence_amd import ops
+    cpu, gpu = torch.device("cpu"), torch.device("cuda", 0)
+    good = torch.zeros(2, 16)
+    ops.check_rows(good, "lse1", 2, 16, cpu)
+    ops.check_rows(None, "dkl", 2, 16, cpu)
+    with pytest.raises(ValueError, match="is on cpu"):
+        ops.check_rows(good, "lse1", 2, 16, gpu)            # host memory for device inputs
+    with pytest.raises(ValueError, match="fp32"):
+        ops.check_rows(good.double(), "kl", 2, 16, cpu)
+    with pytest.raises(ValueError, match="fp32"):
+        ops.check_rows(torch.zeros(2, 15), "kl", 2, 16, cpu)
+    with pytest.raises(ValueError, match="fp32"):
+        ops.check_rows(torch.zeros(16, 2).t(), "dkl", 2, 16, cpu)   # not contiguous
+    with pytest.raises(TypeError):
+        ops.check_rows([0.0] * 32, "lse2", 2, 16, cpu)
+    out = torch.zeros(2, 16, 64)
+    ops.check_out(out, "dq", (2, 16, 64), cpu)
+    with pytest.raises(ValueError, match="is on cpu"):
+        ops.check_out(out, "dq", (2, 16, 64), gpu)
+    with pytest.raises(ValueError, match="fp32"):
+        ops.check_out(torch.zeros(2, 16, 64, dtype=torch.bfloat16), "dk", (2, 16, 64), cpu)
+    with pytest.raises(ValueError, match="fp32"):
+        ops.check_out(torch.zeros(2, 8, 64), "dk", (2, 16, 64), cpu)   # too small
+    with pytest.raises(ValueError, match="fp32"):
+        ops.check_out(torch.zeros(2, 64, 16).transpose(1, 2), "dq", (2, 16, 64), cpu)
+    big = torch.zeros(4, 16, 64)
+    ops.check_disjoint((("dq1", big[:2]), ("dq2", big[2:]), ("dk1", None)))
+    with pytest.raises(ValueError, match="overlap"):
+        ops.check_disjoint((("dq1", big[:3]), ("dq2", big[2:])))

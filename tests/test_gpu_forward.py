@@ -161,3 +161,33 @@ def test_causal8k_config():
         compare(kl[h, rows], rkl, "bf16", f"h{h} kl")
         compare(l1[h, rows], rl1, "bf16", f"h{h} lse1")
         compare(l2[h, rows], rl2, "bf16", f"h{h} lse2")
+
+
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")
+@pytest.mark.parametrize("splits", [None, 4])
+def test_non_finite_inputs_stay_in_their_rows(splits):
+    """One NaN row of Q1 (head 0) and one infinite entry of K2 (head 1, key
+    500): every row whose scores are all finite still matches the oracle, in
+    particular the other queries that share a wave with the NaN row, and the
+    rows that see a non-finite score come out non-finite, as the oracle's do."""
+    need_gpu()
+    heads, n_q, n_k, d = 2, 300, 700, 128
+    log(f"case non-finite inputs, {heads}x{n_q}x{n_k} d={d} causal, splits={splits}")
+    arrs = _rand_case(77, heads, n_q, n_k, d, "bf16")
+    arrs[0][0, 37, :] = np.nan
+    arrs[3][1, 500, 5] = np.inf
+    scale = 1 / np.sqrt(d)
+    kl, l1, l2 = _run_fwd(arrs, "bf16", scale, True, splits)
+    rkl, rl1, rl2 = oracle.forward(*arrs, scale, True)
+    bad = ~(np.isfinite(rkl) & np.isfinite(rl1) & np.isfinite(rl2))
+    # the rows the planted values reach: row 37 of head 0; head 1's rows that see key 500
+    expect = np.zeros_like(bad)
+    expect[0, 37] = True
+    expect[1, 500 - (n_k - n_q):] = True
+    assert np.array_equal(bad, expect)
+    got_bad = ~(np.isfinite(kl) & np.isfinite(l1) & np.isfinite(l2))
+    assert np.array_equal(got_bad, expect), np.argwhere(got_bad != expect)[:10].tolist()
+    ok = ~expect
+    compare(l1[ok], rl1[ok], "bf16", "finite rows lse1")
+    compare(l2[ok], rl2[ok], "bf16", "finite rows lse2")
+    compare(kl[ok], rkl[ok], "bf16", "finite rows kl")

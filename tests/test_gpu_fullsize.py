@@ -2,18 +2,21 @@
 configuration the benchmark times.
 
 * 64K causal (32 heads, N_Q = N_K = 65536, d = 128, bf16, correlated student):
-  forward on every row of head 0 and on sampled rows of every head (first and
-  last 256 rows, rows around query-tile boundaries, seeded random rows); both
-  backward settings through the dK-only and dQ-only launches: dQ on sampled
-  rows of heads 0 and 31, dK on sampled keys of head 0 (from the oracle's own
-  per-row statistics of that head), and on every head the identities
-  sum_j dK_j = 0 and sum_i q_i . dQ_i = sum_j k_j . dK_j; the both-settings
-  launches (the benchmark's) against those, element by element.
+  forward on every row of heads 0 and 31 and on sampled rows of every other
+  head (first and last rows, rows around query-tile boundaries, seeded random
+  rows); both backward settings through the dK-only and dQ-only launches: dQ
+  on sampled rows of heads 0 and 31, dK on sampled keys of head 0 (from the
+  oracle's own per-row statistics of that head), and on every head the
+  identities sum_j dK_j = 0 and sum_i q_i . dQ_i = sum_j k_j . dK_j; the
+  both-settings launches (the benchmark's) against those, element by element;
+  and complete 128-key dK blocks and 128-query dQ blocks (first, middle,
+  last) of heads 0 and 31 against the oracle, for both kernel families.
 * 512K-key decode (32 heads, one query): split-K with the automatic split count
   and with explicit counts, and the single-pass kernel, all heads.
 * 128K non-causal (32 heads): forward on sampled rows of every head; Setting 2
-  dQ on sampled rows of heads 0 and 31, dK on sampled keys of head 0, and the
-  identities on every head.
+  dQ on sampled rows of heads 0 and 31, dK on sampled keys of head 0, the
+  identities on every head, and complete 128-key dK and 128-query dQ blocks
+  (first, middle, last) of heads 0 and 31.
 
 The oracle never sees a GPU value: its inputs are the seeded generators' arrays.
 """
@@ -103,22 +106,29 @@ def causal64k():
     grads["both1"] = (dq2, dk2)
     grads["both2"] = (dq1, dk1)
     torch.cuda.synchronize()
-    log("causal64k: GPU done; oracle head 0 (all rows)")
+    log("causal64k: GPU done; oracle heads 0 and 31 (all rows)")
     a0 = head64(w, 0)
     state0 = _oracle_forward(a0, w, np.arange(w.n_q))
-    log("causal64k: oracle head 0 done")
-    return w, dev, (kl, l1, l2), grads, a0, state0
+    a31 = head64(w, w.heads - 1)
+    state31 = _oracle_forward(a31, w, np.arange(w.n_q))
+    log("causal64k: oracle heads 0 and 31 done")
+    return w, dev, (kl, l1, l2), grads, a0, state0, {0: (a0, state0), w.heads - 1: (a31, state31)}
 
 
 def test_causal64k_forward(causal64k):
-    w, dev, (kl, l1, l2), _, _, state0 = causal64k
+    w, dev, (kl, l1, l2), _, _, state0, full = causal64k
     kl, l1, l2 = [t.cpu().numpy() for t in (kl, l1, l2)]
     rkl, rl1, rl2 = state0
     compare(l1[0], rl1, "bf16", "h0 lse1")
     compare(l2[0], rl2, "bf16", "h0 lse2")
     compare(kl[0], rkl, "bf16", "h0 kl")
+    rkl, rl1, rl2 = full[w.heads - 1][1]
+    h = w.heads - 1
+    compare(l1[h], rl1, "bf16", f"h{h} lse1")
+    compare(l2[h], rl2, "bf16", f"h{h} lse2")
+    compare(kl[h], rkl, "bf16", f"h{h} kl")
     rng = np.random.default_rng(21)
-    for h in range(1, w.heads):
+    for h in range(1, w.heads - 1):
         rows = _sample_rows(w.n_q, rng, edge=64, boundaries=8, random=64)
         a = head64(w, h)
         rkl, rl1, rl2 = _oracle_forward(a, w, rows)
@@ -130,7 +140,7 @@ def test_causal64k_forward(causal64k):
 
 @pytest.mark.parametrize("setting", [1, 2])
 def test_causal64k_backward(causal64k, setting):
-    w, dev, _, grads, a0, state0 = causal64k
+    w, dev, _, grads, a0, state0, _ = causal64k
     dq, dk = grads[setting]
     # the both-settings launches: the same per-pair arithmetic and accumulation
     # order as the single-setting kernels
@@ -149,6 +159,31 @@ def test_causal64k_backward(causal64k, setting):
     rdk = _oracle_dk(a0, w, setting, keys, state0)
     compare(dk[0, keys].cpu().numpy(), rdk, "bf16", f"setting {setting} h0 dk")
     log(f"causal64k setting {setting}: checked")
+
+
+def _full_blocks(n, block=128):
+    """Complete 128-row blocks: the first, one in the middle, the last."""
+    starts = (0, (n // 2) // block * block, n - block)
+    return [np.arange(s0, s0 + block) for s0 in starts]
+
+
+@pytest.mark.parametrize("setting", [1, 2])
+def test_causal64k_full_blocks(causal64k, setting):
+    """Complete 128-key blocks of dK and complete 128-query blocks of dQ
+    (first, mid-sequence on the causal diagonal, last) on heads 0 and 31,
+    against the oracle, for the single-setting kernels and for the
+    both-settings kernels the benchmark times."""
+    w, dev, _, grads, _, _, full = causal64k
+    for h, (a, state) in full.items():
+        for blk in _full_blocks(w.n_k):
+            rdk = _oracle_dk(a, w, setting, blk, state)
+            for name, (_, dk) in (("single", grads[setting]), ("both", grads[f"both{setting}"])):
+                compare(dk[h, blk].cpu().numpy(), rdk, "bf16", f"{name} setting {setting} h{h} dk[{blk[0]}:+128]")
+        for blk in _full_blocks(w.n_q):
+            rdq = _oracle_dq(a, w, setting, blk)
+            for name, (dq, _) in (("single", grads[setting]), ("both", grads[f"both{setting}"])):
+                compare(dq[h, blk].cpu().numpy(), rdq, "bf16", f"{name} setting {setting} h{h} dq[{blk[0]}:+128]")
+    log(f"causal64k setting {setting}: full blocks of heads 0 and {w.heads - 1} checked")
 
 
 def test_decode512k_splitk():
@@ -207,4 +242,13 @@ def test_noncausal128k_forward_setting2():
     state0 = _oracle_forward(a0, w, np.arange(w.n_q))
     keys = _sample_rows(w.n_k, rng, edge=16, boundaries=4, random=32)
     compare(dk[0, keys].cpu().numpy(), _oracle_dk(a0, w, 2, keys, state0), "bf16", "h0 dk1")
-    log("noncausal128k: setting 2 checked")
+    log("noncausal128k: setting 2 sampled rows checked; full blocks of heads 0 and 31")
+    h31 = w.heads - 1
+    a31 = head64(w, h31)
+    state31 = _oracle_forward(a31, w, np.arange(w.n_q))
+    for h, a, state in ((0, a0, state0), (h31, a31, state31)):
+        for blk in _full_blocks(w.n_k):
+            compare(dk[h, blk].cpu().numpy(), _oracle_dk(a, w, 2, blk, state), "bf16", f"h{h} dk1[{blk[0]}:+128]")
+        for blk in _full_blocks(w.n_q):
+            compare(dq[h, blk].cpu().numpy(), _oracle_dq(a, w, 2, blk), "bf16", f"h{h} dq1[{blk[0]}:+128]")
+    log("noncausal128k: setting 2 full blocks checked")

@@ -48,14 +48,28 @@ MUTANTS = {
     "causal_off_by_one": ("return j <= (rows[:, None] + (n_k - n_q))", "return j < (rows[:, None] + (n_k - n_q))"),
     # teacher logits built from the student's keys
     "s1_operand": ("s1 = scale * (q1[rows] @ k1.T)", "s1 = scale * (q1[rows] @ k2.T)"),
-    # upstream weight ignored in Setting 2
     # dK from saved statistics with the student's LSE in the teacher's log-probabilities
     "state_wrong_lse": ("lp1 = np.where(mask, s1 - lse1[r, None], -np.inf)",
                         "lp1 = np.where(mask, s1 - lse2[r, None], -np.inf)"),
     # dK from saved statistics ignoring the causal mask
     "state_no_mask": ("mask = allowed_mask(r, n_q, n_k, causal, keys)",
                       "mask = allowed_mask(r, n_q, n_k, False, keys)"),
+    # upstream weight ignored in Setting 2
     "set2_drop_g": ("ds = g[:, None] * p1 * (r - kl[:, None])", "ds = p1 * (r - kl[:, None])"),
+    # the full logit gradient without the upstream weights
+    "dlogits_drop_g": ("return _dlogits(setting, mask, lp1, lp2, kl, g)",
+                       "return _dlogits(setting, mask, lp1, lp2, kl, np.ones(n_q))"),
+    # the full logit gradient of the other setting
+    "dlogits_swapped_setting": ("return _dlogits(setting, mask, lp1, lp2, kl, g)",
+                                "return _dlogits(3 - setting, mask, lp1, lp2, kl, g)"),
+    # the full logit gradient with the KL of a different row block (rows shifted by one)
+    "dlogits_wrong_kl": ("return _dlogits(setting, mask, lp1, lp2, kl, g)",
+                         "return _dlogits(setting, mask, lp1, lp2, np.roll(kl, 1), g)"),
+    # multi-head forward reading head 0's keys for every head
+    "multihead_wrong_head": ("forward_head(q1[h], k1[h], q2[h], k2[h], scale, causal)",
+                             "forward_head(q1[h], k1[0], q2[h], k2[h], scale, causal)"),
+    # multi-head backward with head 0's upstream weights for every head
+    "multihead_wrong_g": ("None if dkl is None else dkl[h])", "None if dkl is None else dkl[0])"),
 }
 
 
