@@ -76,7 +76,9 @@ enum {
   STREAMKL_ERR_SCALE = -4,        /* scale not finite or negative */
   STREAMKL_ERR_WORKSPACE = -5,    /* workspace NULL or smaller than streamkl_workspace_bytes */
   STREAMKL_ERR_HIP = -6,          /* a HIP launch reported an error */
-  STREAMKL_ERR_ALIGN = -7         /* an array is not 16-byte aligned */
+  STREAMKL_ERR_ALIGN = -7,        /* an array is not 16-byte aligned */
+  STREAMKL_ERR_TOO_LARGE = -8     /* streamkl_fwd_splitk_noalloc: the partial states would
+                                     exceed STREAMKL_NOALLOC_SCRATCH_BYTES */
 };
 
 /*
@@ -106,6 +108,31 @@ int streamkl_fwd_splitk(const void* q1, const void* k1, const void* q2, const vo
                         streamkl_dtype dtype, int num_splits,
                         float* kl, float* lse1, float* lse2,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Size of the fixed device scratch behind streamkl_fwd_splitk_noalloc. */
+#define STREAMKL_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+/*
+ * Split-K forward that allocates nothing, for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same operation, arguments
+ * (minus the workspace), kernels and results as streamkl_fwd_splitk with the
+ * same num_splits; the partial states go to a fixed scratch array of
+ * STREAMKL_NOALLOC_SCRATCH_BYTES (8 MiB) in the library's device memory, one
+ * per GPU, held until the process ends.  The partial states take
+ * 20 * splits * heads * n_q bytes (splits as streamkl_workspace_bytes(0, ...)
+ * counts them); a call that needs more returns STREAMKL_ERR_TOO_LARGE before
+ * anything is enqueued.  The first call on a device looks the scratch up
+ * (hipGetSymbolAddress) with that device current; no call allocates.
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap on
+ * one GPU (different streams, or different host threads without ordering)
+ * race and must be serialised by the caller.  No clearing is needed between
+ * calls: each call writes every partial state its combine reads.
+ */
+int streamkl_fwd_splitk_noalloc(const void* q1, const void* k1, const void* q2, const void* k2,
+                                int n_q, int n_k, int heads, int head_dim, int causal, float scale,
+                                streamkl_dtype dtype, int num_splits,
+                                float* kl, float* lse1, float* lse2, hipStream_t stream);
 
 /*
  * Backward, Setting 1 (Methodology 2: P1 fixed, gradients to the student).

@@ -9,11 +9,13 @@ LIB_PATH = os.path.join(PKG, "libstreamkl.so")
 
 # status codes (include/streamkl.h)
 OK = 0
-ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_SCALE, ERR_WORKSPACE, ERR_HIP, ERR_ALIGN = -1, -2, -3, -4, -5, -6, -7
+ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_SCALE, ERR_WORKSPACE, ERR_HIP, ERR_ALIGN, ERR_TOO_LARGE = (
+    -1, -2, -3, -4, -5, -6, -7, -8)
+NOALLOC_SCRATCH_BYTES = 8 << 20
 BF16, FP32 = 0, 1
 BWD_AUTO, BWD_FUSED, BWD_SEPARATE, BWD_DK_ONLY, BWD_DQ_ONLY = 0, 1, 2, 3, 4
 
-EXPORTS = ("streamkl_fwd", "streamkl_fwd_splitk", "streamkl_bwd_set1",
+EXPORTS = ("streamkl_fwd", "streamkl_fwd_splitk", "streamkl_fwd_splitk_noalloc", "streamkl_bwd_set1",
            "streamkl_bwd_set2", "streamkl_bwd_both",
            "streamkl_workspace_bytes", "streamkl_splitk_auto", "streamkl_bwd_select", "streamkl_strerror")
 
@@ -26,6 +28,7 @@ _IN = [_P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _I]   # q1 k1 q2 k2 n_q n_k heads
 _SIGS = {
     "streamkl_fwd": (_I, _IN + [_P, _P, _P, _P]),
     "streamkl_fwd_splitk": (_I, _IN + [_I, _P, _P, _P, _P, _Z, _P]),
+    "streamkl_fwd_splitk_noalloc": (_I, _IN + [_I, _P, _P, _P, _P]),
     "streamkl_bwd_set1": (_I, _IN + [_P, _P, _P, _P, _P, _I, _P, _Z, _P]),
     "streamkl_bwd_set2": (_I, _IN + [_P, _P, _P, _P, _P, _P, _I, _P, _Z, _P]),
     "streamkl_bwd_both": (_I, _IN + [_P, _P, _P, _P, _P, _P, _P, _P, _I, _P]),

@@ -165,6 +165,24 @@ int streamkl_fwd_splitk(const void* q1, const void* k1, const void* q2, const vo
                        (float*)workspace, stream);
 }
 
+int streamkl_fwd_splitk_noalloc(const void* q1, const void* k1, const void* q2, const void* k2, int n_q,
+                                int n_k, int heads, int head_dim, int causal, float scale, streamkl_dtype dtype,
+                                int num_splits, float* kl, float* lse1, float* lse2, hipStream_t stream) {
+  int st = check_common(q1, k1, q2, k2, n_q, n_k, heads, head_dim, causal, scale, (int)dtype);
+  if (st) return st;
+  if (!kl || !lse1 || !lse2) return STREAMKL_ERR_NULL;
+  if (num_splits < 0 || num_splits > kMaxSplits) return STREAMKL_ERR_UNSUPPORTED;
+  size_t need = 0;
+  const int splits = splitk_count(n_q, n_k, heads, head_dim, num_splits, &need);
+  if (need > skl::kNoAllocScratchBytes) return STREAMKL_ERR_TOO_LARGE;
+  // The partial kernel writes every (range, head, query) state the combine
+  // reads, so the scratch needs no clearing between calls.
+  float* part = nullptr;
+  if (skl::noalloc_scratch(&part) != hipSuccess) return STREAMKL_ERR_HIP;
+  return splitk_launch(q1, k1, q2, k2, n_q, n_k, heads, head_dim, causal, scale, dtype, splits, kl, lse1, lse2,
+                       part, stream);
+}
+
 int streamkl_bwd_select(int n_q, int n_k, int heads, int head_dim, int causal) {
   (void)n_q;
   (void)n_k;
@@ -300,6 +318,7 @@ const char* streamkl_strerror(int status) {
     case STREAMKL_ERR_WORKSPACE: return "workspace missing or too small";
     case STREAMKL_ERR_HIP: return "HIP launch error";
     case STREAMKL_ERR_ALIGN: return "array not 16-byte aligned";
+    case STREAMKL_ERR_TOO_LARGE: return "split-K partial states exceed the 8 MiB scratch of streamkl_fwd_splitk_noalloc";
     default: return "unknown status";
   }
 }

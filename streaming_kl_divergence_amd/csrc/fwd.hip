@@ -30,6 +30,8 @@
 //   * Each XCD walks a contiguous run of (head, query block) items, one head
 //     at a time (xcd_work_index), so the workgroups resident on an XCD stream
 //     the same K tiles through its L2.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -364,6 +366,37 @@ hipError_t launch_splitk_combine(const FwdParams& p, hipStream_t stream) {
   const int rows = p.heads * p.n_q;
   hipLaunchKernelGGL(splitk_combine_kernel, dim3((rows + 3) / 4), dim3(256), 0, stream, p);
   return hipGetLastError();
+}
+
+// Fixed device scratch for the split-K partial states of the entry point that
+// allocates nothing (streamkl_fwd_splitk_noalloc).  Every GPU the library runs
+// on holds its own copy until the process ends.  In host code `scratch` names
+// a host-side stand-in, not device memory, so kernels only ever receive the
+// device address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+float* g_scratch_ptr[kMaxDevices];   // guarded by g_scratch_mutex
+}  // namespace
+
+hipError_t noalloc_scratch(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    // first call on this device, with it current: look the array up once
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = (float*)ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace skl

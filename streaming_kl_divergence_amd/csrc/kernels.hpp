@@ -36,6 +36,13 @@ hipError_t launch_fwd(const FwdParams& p, int dtype, int head_dim, int nw, bool 
                       hipStream_t stream);
 hipError_t launch_splitk_combine(const FwdParams& p, hipStream_t stream);
 
+// Bytes of the fixed device scratch behind streamkl_fwd_splitk_noalloc (the
+// split-K partial states, 20 bytes per (range, head, query)).
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+// Device address of that scratch on the current device (looked up on the
+// first call per device and kept).
+hipError_t noalloc_scratch(float** out);
+
 // Backward kernel arguments (both settings).
 struct BwdParams {
   const char* q1;

@@ -84,6 +84,24 @@ def test_splitk_validation():
     assert lib.streamkl_workspace_bytes(1, 1, 4096, 2, 128, 0, 0) == 0
 
 
+def test_noalloc_splitk_refuses_more_than_its_scratch():
+    """streamkl_fwd_splitk_noalloc validates like streamkl_fwd_splitk and
+    refuses a problem whose partial states exceed its fixed 8 MiB scratch,
+    before any device call."""
+    lib = L.lib()
+    heads, n_q, n_k, d = 64, 4096, 8192, 128
+    need = lib.streamkl_workspace_bytes(0, n_q, n_k, heads, d, 16, 0)
+    assert need > L.NOALLOC_SCRATCH_BYTES
+    args = [FAKE] * 4 + [n_q, n_k, heads, d, 0, 0.1, L.BF16]
+    assert lib.streamkl_fwd_splitk_noalloc(*args, 16, FAKE, FAKE, FAKE, None) == L.ERR_TOO_LARGE
+    assert b"8 MiB" in lib.streamkl_strerror(L.ERR_TOO_LARGE)
+    assert lib.streamkl_fwd_splitk_noalloc(*args, 16, None, FAKE, FAKE, None) == L.ERR_NULL
+    assert lib.streamkl_fwd_splitk_noalloc(*args, 2000, FAKE, FAKE, FAKE, None) == L.ERR_UNSUPPORTED
+    bad = list(args)
+    bad[7] = 96
+    assert lib.streamkl_fwd_splitk_noalloc(*bad, 16, FAKE, FAKE, FAKE, None) == L.ERR_UNSUPPORTED
+
+
 def test_splitk_auto_is_a_valid_split_count():
     lib = L.lib()
     for n_q, n_k in ((1, 524288), (1, 64), (37, 3000), (65536, 65536)):
@@ -132,7 +150,7 @@ def test_both_settings_validation():
 def test_strerror_covers_every_code():
     lib = L.lib()
     for code in (L.OK, L.ERR_NULL, L.ERR_SHAPE, L.ERR_UNSUPPORTED, L.ERR_SCALE, L.ERR_WORKSPACE, L.ERR_HIP,
-                 L.ERR_ALIGN):
+                 L.ERR_ALIGN, L.ERR_TOO_LARGE):
         assert lib.streamkl_strerror(code) not in (None, b"unknown status")
     assert lib.streamkl_strerror(12345) == b"unknown status"
 
