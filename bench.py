@@ -39,6 +39,10 @@ Usage:
       the calibration probes (libstreamkl_probes.so): a pure bf16 MFMA loop,
       the v_exp_f32 issue rate, a plain 8 GiB HBM read and fp32 atomic adds,
       the measured ceilings beside the published peaks.
+  python bench.py --power
+      board power (the GPU's hwmon sensor) while each kernel of the 64K
+      causal step runs back to back, beside idle power and MFMA probes with
+      realistic operands: ms, watts and joules per call.
   python bench.py --workload decode512k
       the decode line instead: the split-K forward for one query per head,
       rated in GB/s against the HBM peak.
@@ -457,6 +461,116 @@ def sweep_mode(which: str):
         raise SystemExit(f"unknown sweep {which!r}")
 
 
+class PowerSampler:
+    """Board power from the GPU's hwmon sensor (power1_input, microwatts),
+    sampled every 0.1 s in a thread while work runs; median over a window."""
+
+    def __init__(self):
+        import glob
+        import threading
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input"))
+        self.path = paths[0] if paths else None
+        self.samples = []
+        self._stop = False
+        self._th = threading.Thread(target=self._run, daemon=True) if self.path else None
+        if self._th:
+            self._th.start()
+
+    def _run(self):
+        while not self._stop:
+            try:
+                with open(self.path) as f:
+                    self.samples.append((time.time(), int(f.read().strip()) / 1e6))
+            except (OSError, ValueError):
+                pass
+            time.sleep(0.1)
+
+    def median(self, t0: float, t1: float):
+        v = [w for t, w in self.samples if t0 <= t <= t1]
+        return round(float(np.median(v)), 1) if v else None
+
+    def stop(self):
+        self._stop = True
+        if self._th:
+            self._th.join()
+
+
+def _loop_for(fn, seconds: float):
+    """Run fn() back to back for about `seconds`; (ms per call, window start, window end)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    t0 = time.time()
+    n = 0
+    while time.time() - t0 < seconds:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    t1 = time.time()
+    return (t1 - t0) / n * 1e3, t0 + 0.5, t1
+
+
+def power_mode(seconds: float = 5.0):
+    """Board power while each kernel of the 64K causal step runs back to back
+    (forward, the both-settings dK and dQ kernels, and Setting 1's two
+    kernels), beside idle power and the calibration probes' (pure MFMA with
+    realistic operands from registers and from LDS, an exp + FMA vector mix).
+    One JSON line per phase: ms per call, median watts, joules per call."""
+    import torch
+    import streaming_kl_divergence_amd as skl
+    from streaming_kl_divergence_amd import _lib
+    ps = PowerSampler()
+    if ps.path is None:
+        print(json.dumps({"power": "no hwmon power sensor readable"}), flush=True)
+        return
+    time.sleep(1.5)
+    t = time.time()
+    print(json.dumps({"phase": "idle", "watts": ps.median(t - 1.2, t)}), flush=True)
+    w = W.WORKLOADS["causal64k"]
+    q1, k1, q2, k2 = upload(w, min(16, os.cpu_count() or 1))
+    kl, l1, l2 = skl.fwd(q1, k1, q2, k2, w.scale, True)
+    g = [torch.empty(w.heads, w.n_q, w.head_dim, device="cuda") for _ in range(4)]
+    E = w.elements()
+    d = w.head_dim
+    phases = [
+        ("fwd_kernel", 4, lambda: skl.fwd(q1, k1, q2, k2, w.scale, True)),
+        ("bwd_kv_both_kernel", 8, lambda: skl.bwd_both(q1, k1, q2, k2, w.scale, True, l1, l2, kl, path="dk_only",
+                                                       dk1=g[1], dk2=g[3])),
+        ("bwd_q_both_kernel", 8, lambda: skl.bwd_both(q1, k1, q2, k2, w.scale, True, l1, l2, kl, path="dq_only",
+                                                      dq1=g[0], dq2=g[2])),
+        ("bwd_kv_kernel set1", 6, lambda: skl.bwd(1, q1, k1, q2, k2, w.scale, True, l1, l2, path="dk_only", dk=g[1])),
+        ("bwd_q_kernel set1", 6, lambda: skl.bwd(1, q1, k1, q2, k2, w.scale, True, l1, l2, path="dq_only", dq=g[0])),
+    ]
+    for name, k, fn in phases:
+        ms, a, b = _loop_for(fn, seconds)
+        watts = ps.median(a, b)
+        print(json.dumps({"phase": name, "ms": round(ms, 3), "executed_tflops": round(k * d * E / (ms * 1e-3) / 1e12, 1),
+                          "watts": watts, "joules_per_call": round(watts * ms * 1e-3, 2) if watts else None}),
+              flush=True)
+        time.sleep(1.0)
+    del q1, k1, q2, k2, g
+    torch.cuda.empty_cache()
+    P = _lib.probes()
+    T = P.streamkl_probe_threads()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    wg = 4 * cus
+    s = torch.cuda.current_stream().cuda_stream
+    src = torch.randn(wg * T * 128, device="cuda").to(torch.bfloat16)   # 256 bytes per thread
+    sink = torch.empty(wg * T, device="cuda")
+    iters = 4000
+    for name, lds in (("mfma_data_regs", 0), ("mfma_data_lds", 1)):
+        ms, a, b = _loop_for(lambda: P.streamkl_probe_mfma_data(src.data_ptr(), src.numel() * 2, lds, wg, iters,
+                                                                sink.data_ptr(), sink.numel(), s), seconds)
+        tf = wg * 4 * iters * 8 * 32768 / (ms * 1e-3) / 1e12
+        watts = ps.median(a, b)
+        print(json.dumps({"phase": name, "ms": round(ms, 3), "executed_tflops": round(tf, 1), "watts": watts,
+                          "pj_per_flop": round(watts / (tf * 1e12) * 1e12, 3) if watts else None}), flush=True)
+        time.sleep(1.0)
+    ps.stop()
+
+
 def calibrate_mode(reps: int = 5):
     """The calibration probes (libstreamkl_probes.so): a pure bf16 MFMA loop,
     a v_exp_f32 stream, a plain 8 GiB read and fp32 atomic adds into a 1 GiB
@@ -485,6 +599,14 @@ def calibrate_mode(reps: int = 5):
     tf = wg * 4 * iters * 4 * 32768 / (ms * 1e-3) / 1e12
     out["mfma_bf16_tflops"] = round(tf, 1)
     out["mfma_bf16_frac_of_peak"] = round(tf / PEAK_BF16_TFLOPS, 4)
+    # the same with realistic operands (random bf16, changing on every MFMA)
+    src = torch.randn(wg * T * 128, device="cuda").to(torch.bfloat16)
+    for name, lds in (("regs", 0), ("lds", 1)):
+        ms = run(lambda: P.streamkl_probe_mfma_data(src.data_ptr(), src.numel() * 2, lds, wg, 4000, sink.data_ptr(),
+                                                    sink.numel(), s))
+        tf = wg * 4 * 4000 * 8 * 32768 / (ms * 1e-3) / 1e12
+        out[f"mfma_bf16_random_{name}_tflops"] = round(tf, 1)
+    del src
     # v_exp_f32: 8 per lane per trip, 16 waves per CU
     iters = 20000
     ms = run(lambda: P.streamkl_probe_exp(wg, iters, sink.data_ptr(), sink.numel(), s))
@@ -633,6 +755,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
                     help="run the calibration probes (MFMA loop, v_exp_f32, HBM read, fp32 atomics)")
+    ap.add_argument("--power", action="store_true",
+                    help="board power while each kernel of the 64K causal step runs back to back, and probes")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--sq-summary", nargs="+", metavar="DIR")
     ap.add_argument("--bwd-path", choices=("both", "separate"), default="both",
@@ -662,6 +786,9 @@ def main():
         del src, dst
     if args.calibrate:
         calibrate_mode()
+        return
+    if args.power:
+        power_mode()
         return
     if args.configs:
         configs_mode()

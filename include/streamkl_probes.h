@@ -8,6 +8,9 @@
  * attention-KL kernels are compared with:
  *   streamkl_probe_mfma    bf16 matrix-core rate (v_mfma_f32_32x32x16_bf16,
  *                          32768 flop per wave instruction, 4 per loop trip);
+ *   streamkl_probe_mfma_data  the same with realistic operands (caller data,
+ *                          changing on every instruction), from registers or
+ *                          with the A operand from LDS;
  *   streamkl_probe_exp     v_exp_f32 issue rate (8 per lane per loop trip);
  *   streamkl_probe_read    HBM read rate (16-byte loads, grid-stride);
  *   streamkl_probe_atomic  fp32 atomic-add rate (4-byte payload per add).
@@ -32,6 +35,13 @@ int streamkl_probe_threads(void);
 /* workgroups x 4 waves, each `iters` trips of 4 independent MFMAs on register
  * operands.  sink: >= workgroups * threads floats (written, meaningless). */
 int streamkl_probe_mfma(int workgroups, int iters, float* sink, size_t sink_floats, hipStream_t stream);
+
+/* As streamkl_probe_mfma, but each lane cycles through 8 A and 8 B operand
+ * chunks read from src (src_bytes >= workgroups * threads * 256, 16-byte
+ * aligned); from_lds != 0 takes the A operand from a 32 KB LDS tile of that
+ * data instead.  8 MFMAs of 32768 flop per wave per loop trip. */
+int streamkl_probe_mfma_data(const void* src, size_t src_bytes, int from_lds, int workgroups, int iters, float* sink,
+                             size_t sink_floats, hipStream_t stream);
 
 /* workgroups x 256 threads, each `iters` trips of 8 independent v_exp_f32.
  * sink: >= workgroups * threads floats. */

@@ -205,12 +205,8 @@ struct TileStream {
   }
   __device__ __forceinline__ void init(int tid) { voff0 = lane_off(0, tid); }
 
-  __device__ __forceinline__ void issue(const char* __restrict__ g, int key0, int n_rows, SKL_LDS char* tile,
-                                        int tid, int wave) const {
-    if (key0 + BK > n_rows) {
-      issue_tile_async<T, D, BK, NW>(g, key0, n_rows, tile, tid, wave);
-      return;
-    }
+  __device__ __forceinline__ void issue_full(const char* __restrict__ g, int key0, SKL_LDS char* tile, int tid,
+                                             int wave) const {
     const char* base = g + (size_t)key0 * G::kRowBytes;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
@@ -220,6 +216,30 @@ struct TileStream {
       else
         lds_dma_16_sbase(base, lane_off(i, tid), lb);
     }
+  }
+
+  __device__ __forceinline__ void issue(const char* __restrict__ g, int key0, int n_rows, SKL_LDS char* tile,
+                                        int tid, int wave) const {
+    if (key0 + BK > n_rows) {
+      issue_tile_async<T, D, BK, NW>(g, key0, n_rows, tile, tid, wave);
+      return;
+    }
+    issue_full(g, key0, tile, tid, wave);
+  }
+
+  // The same rows of two tensors (K1 and K2, or Q1 and Q2) into two tiles,
+  // under one test for the clamped last tile, so that the clamped path's
+  // per-lane address work stays inside that (rare) branch.
+  __device__ __forceinline__ void issue2(const char* __restrict__ g1, const char* __restrict__ g2, int key0,
+                                         int n_rows, SKL_LDS char* tile1, SKL_LDS char* tile2, int tid,
+                                         int wave) const {
+    if (__builtin_expect(key0 + BK > n_rows, 0)) {
+      issue_tile_async<T, D, BK, NW>(g1, key0, n_rows, tile1, tid, wave);
+      issue_tile_async<T, D, BK, NW>(g2, key0, n_rows, tile2, tid, wave);
+      return;
+    }
+    issue_full(g1, key0, tile1, tid, wave);
+    issue_full(g2, key0, tile2, tid, wave);
   }
 };
 

@@ -30,6 +30,8 @@
 //   * Each XCD walks a contiguous run of (head, query block) items, one head
 //     at a time (xcd_work_index), so the workgroups resident on an XCD stream
 //     the same K tiles through its L2.
+#include <limits.h>
+
 #include <mutex>
 
 #include "common.hpp"
@@ -37,9 +39,12 @@
 
 namespace skl {
 
-// Running five-scalar state of one lane (one query, half of the keys).
+// Running five-scalar state of one lane (one query, half of the keys), with
+// the exponent offsets -m1 c and -m2 c kept beside the maxima (they change
+// only when a maximum does).
 struct RowState {
   float m1, m2, l1, l2, acc;
+  float nmc1, nmc2;
 };
 
 // S1, S2 (raw units) of one 64-key tile for this lane's query: 2 blocks of 16.
@@ -89,15 +94,16 @@ __device__ __forceinline__ void tile_update(RowState& st, f32x16* s1, f32x16* s2
   const float a1 = fast_exp2((st.m1 - n1) * c), a2 = fast_exp2((st.m2 - n2) * c);
   st.m1 = n1;
   st.m2 = n2;
-  const float mc1 = n1 * c, mc2 = n2 * c;
-  float sl1[4] = {0.f, 0.f, 0.f, 0.f}, sl2[4] = {0.f, 0.f, 0.f, 0.f}, sa[4] = {0.f, 0.f, 0.f, 0.f};
+  st.nmc1 = -(n1 * c);
+  st.nmc2 = -(n2 * c);
+  float sl1[4], sl2[4], sa[4];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float x1 = s1[kb][r], x2 = s2[kb][r];
-      float e1 = fast_exp2(fmaf(x1, c, -mc1));
-      float e2 = fast_exp2(fmaf(x2, c, -mc2));
+      float e1 = fast_exp2(fmaf(x1, c, st.nmc1));
+      float e2 = fast_exp2(fmaf(x2, c, st.nmc2));
       float d = x1 - x2;
       if (MASK) {
         const bool ok = x1 != -INFINITY;  // real scores are finite
@@ -106,9 +112,15 @@ __device__ __forceinline__ void tile_update(RowState& st, f32x16* s1, f32x16* s2
         d = ok ? d : 0.f;
       }
       const int j = r & 3;
-      sl1[j] += e1;
-      sl2[j] += e2;
-      sa[j] = fmaf(e1, d, sa[j]);
+      if (kb == 0 && r < 4) {   // the first term of each partial sum starts it
+        sl1[j] = e1;
+        sl2[j] = e2;
+        sa[j] = e1 * d;
+      } else {
+        sl1[j] += e1;
+        sl2[j] += e2;
+        sa[j] = fmaf(e1, d, sa[j]);
+      }
     }
   st.l1 = fmaf(a1, st.l1, (sl1[0] + sl1[1]) + (sl1[2] + sl1[3]));
   st.l2 = fmaf(a2, st.l2, (sl2[0] + sl2[1]) + (sl2[2] + sl2[3]));
@@ -131,23 +143,30 @@ __device__ __forceinline__ void tile_update(RowState& st, f32x16* s1, f32x16* s2
 // row exact.
 template <int NKB>
 __device__ __forceinline__ bool tile_fold_at_offsets(RowState& st, const f32x16* s1, const f32x16* s2, float c) {
-  const float mc1 = st.m1 * c, mc2 = st.m2 * c;
-  float sl1[4] = {0.f, 0.f, 0.f, 0.f}, sl2[4] = {0.f, 0.f, 0.f, 0.f}, sa[4] = {0.f, 0.f, 0.f, 0.f};
+  float sl1[4], sl2[4], sa[4];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float x1 = s1[kb][r], x2 = s2[kb][r];
       const int j = r & 3;
-      const float e1 = fast_exp2(fmaf(x1, c, -mc1));
-      sl1[j] += e1;
-      sl2[j] += fast_exp2(fmaf(x2, c, -mc2));
-      sa[j] = fmaf(e1, x1 - x2, sa[j]);
+      const float e1 = fast_exp2(fmaf(x1, c, st.nmc1));
+      const float e2 = fast_exp2(fmaf(x2, c, st.nmc2));
+      if (kb == 0 && r < 4) {   // the first term of each partial sum starts it
+        sl1[j] = e1;
+        sl2[j] = e2;
+        sa[j] = e1 * (x1 - x2);
+      } else {
+        sl1[j] += e1;
+        sl2[j] += e2;
+        sa[j] = fmaf(e1, x1 - x2, sa[j]);
+      }
     }
   const float t1 = (sl1[0] + sl1[1]) + (sl1[2] + sl1[3]);
   const float t2 = (sl2[0] + sl2[1]) + (sl2[2] + sl2[3]);
-  const bool fits = (t1 < 0x1p64f) & (t2 < 0x1p64f);   // false for inf and NaN too
-  if (__builtin_amdgcn_ballot_w64(!fits) != 0) return false;
+  // the comparisons are false for inf and NaN too
+  const uint64_t bad = __builtin_amdgcn_ballot_w64(!(t1 < 0x1p64f)) | __builtin_amdgcn_ballot_w64(!(t2 < 0x1p64f));
+  if (bad != 0) return false;
   st.l1 += t1;
   st.l2 += t2;
   st.acc += (sa[0] + sa[1]) + (sa[2] + sa[3]);
@@ -226,7 +245,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
     }
   }
 
-  RowState st{kMaxInit, kMaxInit, 0.f, 0.f, 0.f};
+  RowState st{kMaxInit, kMaxInit, 0.f, 0.f, 0.f, -(kMaxInit * p.c), -(kMaxInit * p.c)};
   const float c = p.c;
   const int qlim = qrow + off;   // last key this lane's query may see (causal)
   const int pb = pair_base<T, D>(col, h);
@@ -239,21 +258,27 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
     issue_tile_async<T, D, BK, NW>(k1, kbeg, p.n_k, lds, tid, wave);
     issue_tile_async<T, D, BK, NW>(k2, kbeg, p.n_k, lds + TILE, tid, wave);
   }
+  // The last key this wave's first query may see: a tile holding a key past
+  // it crosses the causal diagonal (wave-uniform).
+  const int wdiag = p.causal ? qw0 + off : INT_MAX;
   for (int t = 0; t < ntiles; ++t) {
     wait_async_loads();
     __syncthreads();  // tile t visible; buffer t+1 free again
     const int buf = t & 1;
     if (t + 1 < ntiles) {
       SKL_LDS char* nb = lds + (buf ^ 1) * 2 * TILE;
-      ts.issue(k1, kbeg + (t + 1) * BK, p.n_k, nb, tid, wave);
-      ts.issue(k2, kbeg + (t + 1) * BK, p.n_k, nb + TILE, tid, wave);
+      ts.issue2(k1, k2, kbeg + (t + 1) * BK, p.n_k, nb, nb + TILE, tid, wave);
     }
     if (t >= wtiles) continue;
     const int k0 = kbeg + t * BK;
-    const bool need_mask = (k0 + BK > klimit) || (p.causal && k0 + BK - 1 > qw0 + off);
-    const SKL_LDS char* cur = lds + buf * 2 * TILE;
+    const bool need_mask = (k0 + BK > klimit) | (k0 + BK - 1 > wdiag);
+    // one copy of the MFMA phase per LDS buffer, so that each operand address
+    // is a per-lane base plus an immediate offset
     __builtin_amdgcn_s_setprio(1);   // MFMA phase first when two waves share a SIMD
-    tile_scores<T, D, NKB>(cur, cur + TILE, qf1, qf2, pb, s1, s2);
+    if (buf)
+      tile_scores<T, D, NKB>(lds + 2 * TILE, lds + 3 * TILE, qf1, qf2, pb, s1, s2);
+    else
+      tile_scores<T, D, NKB>(lds, lds + TILE, qf1, qf2, pb, s1, s2);
     __builtin_amdgcn_s_setprio(0);
     if (need_mask) {
       tile_update<true, NKB>(st, s1, s2, c, k0, h, klimit, p.causal, qlim);

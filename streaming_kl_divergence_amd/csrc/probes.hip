@@ -14,6 +14,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 
@@ -34,6 +35,56 @@ __global__ __launch_bounds__(kThreads) void mfma_loop(int iters, float* __restri
     c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c1, 0, 0, 0);
     c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, a, c2, 0, 0, 0);
     c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, b, c3, 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  sink[gid] = s;
+}
+
+// The same MFMA loop with realistic operands: each lane holds 8 different A
+// and B chunks loaded from `src` (caller-supplied data, 256 bytes per thread),
+// so the multiplier inputs change on every instruction as they do on real
+// tiles.  LDS = true: the A operand comes from a 32 KB LDS tile of the same
+// data instead (16 bytes per lane per MFMA, the score-MFMA access pattern).
+template <bool LDS>
+__global__ __launch_bounds__(kThreads) void mfma_data_loop(const u32x4* __restrict__ src, int iters,
+                                                          float* __restrict__ sink) {
+  __shared__ u32x4 tile[LDS ? 2048 : 1];
+  const int gid = blockIdx.x * kThreads + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  u32x4 a[8], b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = src[(size_t)gid * 16 + i];
+    b[i] = src[(size_t)gid * 16 + 8 + i];
+  }
+  if (LDS) {
+    // this workgroup's 256 threads x 256 bytes = 64 KB of src; its first 32 KB fill the tile
+    for (int i = threadIdx.x; i < 2048; i += kThreads) tile[i] = src[(size_t)blockIdx.x * kThreads * 16 + i];
+    __syncthreads();
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; i += 4) {
+      u32x4 x0 = a[i], x1 = a[i + 1], x2 = a[i + 2], x3 = a[i + 3];
+      if (LDS) {
+        const int o = (it * 8 + i) * 64 + lane;
+        x0 = tile[o & 2047];
+        x1 = tile[(o + 64) & 2047];
+        x2 = tile[(o + 128) & 2047];
+        x3 = tile[(o + 192) & 2047];
+      }
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x0), __builtin_bit_cast(bf16x8, b[i]),
+                                                    c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x1),
+                                                    __builtin_bit_cast(bf16x8, b[i + 1]), c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x2),
+                                                    __builtin_bit_cast(bf16x8, b[i + 2]), c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x3),
+                                                    __builtin_bit_cast(bf16x8, b[i + 3]), c3, 0, 0, 0);
+    }
   }
   float s = 0.f;
 #pragma unroll
@@ -99,6 +150,20 @@ int streamkl_probe_threads(void) { return kThreads; }
 int streamkl_probe_mfma(int workgroups, int iters, float* sink, size_t sink_floats, hipStream_t stream) {
   if (workgroups < 1 || iters < 1 || !sink || sink_floats < (size_t)workgroups * kThreads) return -1;
   hipLaunchKernelGGL(mfma_loop, dim3(workgroups), dim3(kThreads), 0, stream, iters, sink);
+  return status(hipGetLastError());
+}
+
+int streamkl_probe_mfma_data(const void* src, size_t src_bytes, int from_lds, int workgroups, int iters, float* sink,
+                             size_t sink_floats, hipStream_t stream) {
+  if (!src || workgroups < 1 || iters < 1 || !sink || sink_floats < (size_t)workgroups * kThreads ||
+      ((uintptr_t)src & 15) != 0 || src_bytes < (size_t)workgroups * kThreads * 256)
+    return -1;
+  if (from_lds)
+    hipLaunchKernelGGL(mfma_data_loop<true>, dim3(workgroups), dim3(kThreads), 0, stream, (const u32x4*)src, iters,
+                       sink);
+  else
+    hipLaunchKernelGGL(mfma_data_loop<false>, dim3(workgroups), dim3(kThreads), 0, stream, (const u32x4*)src, iters,
+                       sink);
   return status(hipGetLastError());
 }
 
