@@ -22,8 +22,9 @@ operands under the board power limit, the HBM read rate, fp32 atomics) come from
 (hipBLASLt) as platform context (parts.gemm_bf16_16384_tflops).
 
 Usage:
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--gemm-ref]
-      the one-line benchmark of the 64K causal step (the default).
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--gemm-ref] [--no-decode]
+      the one-line benchmark of the 64K causal step (the default); parts.decode512k
+      carries the 512K-key split-K decode's HBM read rate, timed in the same run.
   python bench.py --configs
       one JSON line per workload (tiny fp32, 8K causal, 64K causal with both
       backward paths and the both-settings backward, 512K decode split-K vs
@@ -666,6 +667,28 @@ def cpu_baseline():
                       f"Setting 2, fp64 numpy/BLAS; {dt:.1f} s for {flop / 1e12:.3f} TFLOP"}
 
 
+def decode_part(reps: int = 20) -> dict:
+    """The 512K-key decode workload (32 heads, one query, split-K with the
+    automatic count) timed beside the step: HBM read rate of its inputs."""
+    import torch
+    import streaming_kl_divergence_amd as skl
+    w = W.WORKLOADS["decode512k"]
+    q1, k1, q2, k2 = upload(w, min(16, os.cpu_count() or 1))
+    d = w.head_dim
+    ws = torch.empty(max(16, skl.splitk_workspace_bytes(w.n_q, w.n_k, w.heads, d, 0)), device="cuda",
+                     dtype=torch.uint8)
+    t = _timed(lambda: skl.fwd_splitk(q1, k1, q2, k2, w.scale, w.causal, 0, ws), torch.cuda.current_stream(), 3,
+               reps)
+    ms = float(np.mean(t))
+    byts = 2 * w.heads * (w.n_k + w.n_q) * d * 2
+    gbs = byts / (ms * 1e-3) / 1e9
+    del q1, k1, q2, k2, ws
+    torch.cuda.empty_cache()
+    return {"ms": round(ms, 4), "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "splits": skl.splitk_auto(w.n_q, w.n_k, w.heads, d),
+            "work": "split-K forward, 32 heads x 1 query x 524288 keys, d=128, bf16: K1, K2, Q1, Q2 read once"}
+
+
 def decode_mode(w: W.Workload, args, inputs, t_up: float):
     """One query per head (decode): one step is the split-K forward with the
     library's automatic split count, the partial kernel and then the combine
@@ -751,6 +774,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gemm-ref", action="store_true", help="also time a 16384^3 bf16 GEMM (torch.mm) as context")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the 512K-key split-K decode measured beside the step (parts.decode512k)")
     ap.add_argument("--no-gemm-ref", action="store_true", help=argparse.SUPPRESS)   # the default; kept for old commands
     ap.add_argument("--workload", default="causal64k")
     ap.add_argument("--configs", action="store_true")
@@ -899,6 +924,8 @@ def main():
         parts["gemm_bf16_16384_tflops"] = round(gemm, 1)
     parts["wall_s_timed"] = round(wall, 3)
     parts["upload_s"] = round(t_up, 1)
+    if not args.no_decode:
+        parts["decode512k"] = decode_part()
 
     # dominant kernel: the single launch with the largest mean duration
     j = int(np.argmax(mean_call))
