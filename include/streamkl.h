@@ -45,6 +45,21 @@
  *     n_q, n_k, heads >= 1 with heads * n_q and heads * n_k below 2^31 rows.
  *   Thread safety: calls may be made from several host threads; calls that
  *     write the same outputs must be ordered by the caller.
+ *   Environment (read once per process, at the first call that needs it; for
+ *     experiments, the arguments stay the interface):
+ *     STREAMKL_LOG=1     one line on stderr per compute call: its shape, what
+ *                        was chosen (split count and its source, backward
+ *                        path, workgroup counts) and the status returned.
+ *     STREAMKL_SPLITS=n  the split count num_splits = 0 resolves to
+ *                        (1 <= n <= 1024, then reduced to the non-empty key
+ *                        ranges); streamkl_splitk_auto and
+ *                        streamkl_workspace_bytes report it too.
+ *     STREAMKL_BWD_PATH=fused|separate  the path STREAMKL_BWD_AUTO resolves
+ *                        to in streamkl_bwd_set1/2 and streamkl_bwd_select
+ *                        (fused falls back to separate where unsupported);
+ *                        streamkl_bwd_both has no fused variant and ignores it.
+ *     A value that does not parse is ignored with a warning on stderr.  Tile
+ *     shapes are compile-time constants of the kernels and have no override.
  */
 #ifndef STREAMKL_H
 #define STREAMKL_H
@@ -198,7 +213,8 @@ int streamkl_bwd_both(const void* q1, const void* k1, const void* q2, const void
 size_t streamkl_workspace_bytes(int op, int n_q, int n_k, int heads, int head_dim,
                                 int num_splits, streamkl_bwd_path path);
 
-/* The split count streamkl_fwd_splitk uses when num_splits = 0. */
+/* The split count streamkl_fwd_splitk uses when num_splits = 0 (the
+ * heuristic, or STREAMKL_SPLITS when set). */
 int streamkl_splitk_auto(int n_q, int n_k, int heads, int head_dim);
 
 /* The backward path AUTO resolves to for this shape (STREAMKL_BWD_FUSED or
@@ -208,8 +224,9 @@ int streamkl_splitk_auto(int n_q, int n_k, int heads, int head_dim);
  * fp32 atomics per (query, key) pair and was measured slower than the separate
  * kernels at every size tried (64 to 16K queries against 128K keys, both
  * settings), so the result does not depend on the arguments: it is
- * STREAMKL_BWD_SEPARATE for every shape.  The arguments are kept so that a
- * shape-dependent rule can be added without changing the ABI. */
+ * STREAMKL_BWD_SEPARATE for every shape, unless STREAMKL_BWD_PATH is set.
+ * The arguments are kept so that a shape-dependent rule can be added without
+ * changing the ABI. */
 int streamkl_bwd_select(int n_q, int n_k, int heads, int head_dim, int causal);
 
 /* Static text for a status code. */
