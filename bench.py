@@ -530,7 +530,8 @@ def power_mode(seconds: float = 5.0):
         return
     time.sleep(1.5)
     t = time.time()
-    print(json.dumps({"phase": "idle", "watts": ps.median(t - 1.2, t)}), flush=True)
+    idle = ps.median(t - 1.2, t)
+    print(json.dumps({"phase": "idle", "watts": idle}), flush=True)
     w = W.WORKLOADS["causal64k"]
     q1, k1, q2, k2 = upload(w, min(16, os.cpu_count() or 1))
     kl, l1, l2 = skl.fwd(q1, k1, q2, k2, w.scale, True)
@@ -550,7 +551,8 @@ def power_mode(seconds: float = 5.0):
         ms, a, b = _loop_for(fn, seconds)
         watts = ps.median(a, b)
         print(json.dumps({"phase": name, "ms": round(ms, 3), "executed_tflops": round(k * d * E / (ms * 1e-3) / 1e12, 1),
-                          "watts": watts, "joules_per_call": round(watts * ms * 1e-3, 2) if watts else None}),
+                          "watts": watts, "joules_per_call": round(watts * ms * 1e-3, 2) if watts else None,
+                          "dynamic_joules_per_call": round((watts - idle) * ms * 1e-3, 2) if watts and idle else None}),
               flush=True)
         time.sleep(1.0)
     del q1, k1, q2, k2, g
@@ -558,27 +560,31 @@ def power_mode(seconds: float = 5.0):
     P = _lib.probes()
     T = P.streamkl_probe_threads()
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    wg = 4 * cus
     s = torch.cuda.current_stream().cuda_stream
-    src = torch.randn(wg * T * 128, device="cuda").to(torch.bfloat16)   # 256 bytes per thread
-    sink = torch.empty(wg * T, device="cuda")
-    iters = 4000
-    for name, lds in (("mfma_data_regs", 0), ("mfma_data_lds", 1)):
-        ms, a, b = _loop_for(lambda: P.streamkl_probe_mfma_data(src.data_ptr(), src.numel() * 2, lds, wg, iters,
+    src = torch.randn(3 * cus * T * 128, device="cuda").to(torch.bfloat16)   # 256 bytes per thread
+    sink = torch.empty(3 * cus * T, device="cuda")
+    # one workgroup per CU per wave-per-SIMD, all resident at once; ~10 ms calls
+    for name, lds, wps in (("mfma_data_regs", 0, 1), ("mfma_data_regs", 0, 2), ("mfma_data_regs", 0, 3),
+                           ("mfma_data_lds", 1, 1), ("mfma_data_lds", 1, 2)):
+        wg, iters = wps * cus, 75000 // wps
+        ms, a, b = _loop_for(lambda: P.streamkl_probe_mfma_data(src.data_ptr(), src.numel() * 2, lds, wps, wg, iters,
                                                                 sink.data_ptr(), sink.numel(), s), seconds)
         tf = wg * 4 * iters * 8 * 32768 / (ms * 1e-3) / 1e12
         watts = ps.median(a, b)
-        print(json.dumps({"phase": name, "ms": round(ms, 3), "executed_tflops": round(tf, 1), "watts": watts,
-                          "pj_per_flop": round(watts / (tf * 1e12) * 1e12, 3) if watts else None}), flush=True)
+        print(json.dumps({"phase": f"{name} {wps} wave(s)/SIMD", "ms": round(ms, 3), "executed_tflops": round(tf, 1),
+                          "watts": watts,
+                          "dynamic_pj_per_flop": round((watts - idle) / tf, 3) if watts and idle else None}),
+              flush=True)
         time.sleep(1.0)
     ps.stop()
 
 
-def calibrate_mode(reps: int = 5):
-    """The calibration probes (libstreamkl_probes.so): a pure bf16 MFMA loop,
-    a v_exp_f32 stream, a plain 8 GiB read and fp32 atomic adds into a 1 GiB
-    and a 2 MiB buffer.  One JSON line; rates are medians of `reps` timed runs.
-    Cycle figures assume the nominal 2.4 GHz shader clock."""
+def calibrate_mode(reps: int = 5, mfma_seconds: float = 3.0):
+    """The calibration probes (libstreamkl_probes.so): bf16 MFMA loops at 1 to
+    3 waves per SIMD (sustained, with board watts), a v_exp_f32 stream, a plain
+    8 GiB read and fp32 atomic adds into a 1 GiB and a 2 MiB buffer.  One JSON
+    line; the other rates are medians of `reps` timed runs.  Cycle figures
+    assume the nominal 2.4 GHz shader clock."""
     import torch
     from streaming_kl_divergence_amd import _lib
     P = _lib.probes()
@@ -595,23 +601,40 @@ def calibrate_mode(reps: int = 5):
         return float(np.median(_timed(f, stream, 2, reps)))
 
     out = {"probe": "calibration", "compute_units": cus, "nominal_clock_ghz": clk / 1e9}
-    # matrix cores: 16 waves per CU (4 per SIMD), 4 MFMAs of 32768 flop per trip
-    wg, iters = 4 * cus, 20000
-    sink = torch.empty(wg * T, device="cuda")
-    ms = run(lambda: P.streamkl_probe_mfma(wg, iters, sink.data_ptr(), sink.numel(), s))
-    tf = wg * 4 * iters * 4 * 32768 / (ms * 1e-3) / 1e12
-    out["mfma_bf16_tflops"] = round(tf, 1)
-    out["mfma_bf16_frac_of_peak"] = round(tf / PEAK_BF16_TFLOPS, 4)
-    # the same with realistic operands (random bf16, changing on every MFMA)
-    src = torch.randn(wg * T * 128, device="cuda").to(torch.bfloat16)
-    for name, lds in (("regs", 0), ("lds", 1)):
-        ms = run(lambda: P.streamkl_probe_mfma_data(src.data_ptr(), src.numel() * 2, lds, wg, 4000, sink.data_ptr(),
-                                                    sink.numel(), s))
-        tf = wg * 4 * 4000 * 8 * 32768 / (ms * 1e-3) / 1e12
-        out[f"mfma_bf16_random_{name}_tflops"] = round(tf, 1)
+    ps = PowerSampler()
+    # Matrix cores, sustained (each probe runs back to back for `mfma_seconds`,
+    # long enough for the board to settle at its power limit), at 1, 2 and 3
+    # waves per SIMD: one workgroup per CU per wave-per-SIMD, all resident at
+    # once, ~10 ms per call.  Constant operands, then realistic ones (random
+    # bf16 changing on every MFMA) from registers and with A from LDS.
+    wg_max = 4 * cus
+    sink = torch.empty(wg_max * T, device="cuda")
+    src = torch.randn(wg_max * T * 128, device="cuda").to(torch.bfloat16)   # 256 bytes per thread
+    best = 0.0
+    for kind, per_trip, base_iters in (("const", 4, 150000), ("random_regs", 8, 75000), ("random_lds", 8, 75000)):
+        for wps in (1, 2, 3):
+            wg, iters = wps * cus, base_iters // wps
+            if kind == "const":
+                launch = lambda: P.streamkl_probe_mfma(wps, wg, iters, sink.data_ptr(), sink.numel(), s)
+            else:
+                lds = int(kind == "random_lds")
+                launch = lambda: P.streamkl_probe_mfma_data(src.data_ptr(), src.numel() * 2, lds, wps, wg, iters,
+                                                            sink.data_ptr(), sink.numel(), s)
+            if launch() != 0:
+                raise RuntimeError("probe launch failed")
+            ms, a, b = _loop_for(launch, mfma_seconds)
+            tf = wg * 4 * iters * per_trip * 32768 / (ms * 1e-3) / 1e12
+            out[f"mfma_bf16_{kind}_w{wps}_tflops"] = round(tf, 1)
+            out[f"mfma_bf16_{kind}_w{wps}_watts"] = ps.median(a, b)
+            if kind != "const":
+                best = max(best, tf)
+            time.sleep(1.0)
+    out["mfma_bf16_random_best_tflops"] = round(best, 1)
+    out["mfma_bf16_random_best_frac_of_peak"] = round(best / PEAK_BF16_TFLOPS, 4)
+    ps.stop()
     del src
     # v_exp_f32: 8 per lane per trip, 16 waves per CU
-    iters = 20000
+    wg, iters = 4 * cus, 20000
     ms = run(lambda: P.streamkl_probe_exp(wg, iters, sink.data_ptr(), sink.numel(), s))
     wave_insts = wg * 4 * iters * 8
     out["exp_wave_insts_per_s"] = wave_insts / (ms * 1e-3)

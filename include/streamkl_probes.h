@@ -32,16 +32,19 @@ extern "C" {
 /* Threads per workgroup of every probe (sink arrays hold one value per thread). */
 int streamkl_probe_threads(void);
 
-/* workgroups x 4 waves, each `iters` trips of 4 independent MFMAs on register
- * operands.  sink: >= workgroups * threads floats (written, meaningless). */
-int streamkl_probe_mfma(int workgroups, int iters, float* sink, size_t sink_floats, hipStream_t stream);
+/* workgroups x 4 waves, each `iters` trips of 4 independent MFMAs on constant
+ * register operands.  waves_per_simd (1 to 3): each workgroup reserves enough
+ * LDS that at most that many share a compute unit, i.e. that many waves per
+ * SIMD.  sink: >= workgroups * threads floats (written, meaningless). */
+int streamkl_probe_mfma(int waves_per_simd, int workgroups, int iters, float* sink, size_t sink_floats,
+                        hipStream_t stream);
 
 /* As streamkl_probe_mfma, but each lane cycles through 8 A and 8 B operand
  * chunks read from src (src_bytes >= workgroups * threads * 256, 16-byte
  * aligned); from_lds != 0 takes the A operand from a 32 KB LDS tile of that
  * data instead.  8 MFMAs of 32768 flop per wave per loop trip. */
-int streamkl_probe_mfma_data(const void* src, size_t src_bytes, int from_lds, int workgroups, int iters, float* sink,
-                             size_t sink_floats, hipStream_t stream);
+int streamkl_probe_mfma_data(const void* src, size_t src_bytes, int from_lds, int waves_per_simd, int workgroups,
+                             int iters, float* sink, size_t sink_floats, hipStream_t stream);
 
 /* workgroups x 256 threads, each `iters` trips of 8 independent v_exp_f32.
  * sink: >= workgroups * threads floats. */

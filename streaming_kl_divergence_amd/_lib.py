@@ -45,8 +45,8 @@ PROBE_EXPORTS = ("streamkl_probe_threads", "streamkl_probe_mfma", "streamkl_prob
                  "streamkl_probe_read", "streamkl_probe_atomic")
 _PROBE_SIGS = {
     "streamkl_probe_threads": (_I, []),
-    "streamkl_probe_mfma": (_I, [_I, _I, _P, _Z, _P]),
-    "streamkl_probe_mfma_data": (_I, [_P, _Z, _I, _I, _I, _P, _Z, _P]),
+    "streamkl_probe_mfma": (_I, [_I, _I, _I, _P, _Z, _P]),
+    "streamkl_probe_mfma_data": (_I, [_P, _Z, _I, _I, _I, _I, _P, _Z, _P]),
     "streamkl_probe_exp": (_I, [_I, _I, _P, _Z, _P]),
     "streamkl_probe_read": (_I, [_P, _Z, _I, _P, _Z, _P]),
     "streamkl_probe_atomic": (_I, [_P, _Z, _I, _I, _P]),

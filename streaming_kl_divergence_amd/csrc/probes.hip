@@ -18,10 +18,32 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 
+// LDS a matrix-core probe workgroup reserves so that at most WPS of them fit in
+// the 160 KB of a CU.  A workgroup is 4 waves, one per SIMD, so WPS is also the
+// number of waves per SIMD (the registers of these kernels allow up to 3).
+// How many waves share a SIMD changes what the matrix cores sustain.
+template <int WPS>
+constexpr int reserve_bytes() {
+  static_assert(WPS >= 1 && WPS <= 3, "1 to 3 waves per SIMD");
+  return WPS == 1 ? 96 * 1024 : WPS == 2 ? 64 * 1024 : 48 * 1024;
+}
+
+// The per-lane result goes through the reserved LDS on its way to sink[gid],
+// so the reservation is part of the kernel and nothing is optimised away.
+template <int WPS>
+__device__ __forceinline__ void store_through_lds(u32x4* lds, float s, float* __restrict__ sink, int gid) {
+  __syncthreads();
+  lds[threadIdx.x] = u32x4{__float_as_uint(s), 0u, 0u, 0u};
+  __syncthreads();
+  sink[gid] = __uint_as_float(lds[(threadIdx.x + 1) % kThreads].x);
+}
+
 // Four independent accumulator chains of v_mfma_f32_32x32x16_bf16 per wave,
 // operands in registers.  One lane's sum of the results goes to sink[gid] so
 // that nothing is optimised away.
+template <int WPS>
 __global__ __launch_bounds__(kThreads) void mfma_loop(int iters, float* __restrict__ sink) {
+  __shared__ u32x4 lds[reserve_bytes<WPS>() / 16];
   const int gid = blockIdx.x * kThreads + threadIdx.x;
   bf16x8 a, b;
 #pragma unroll
@@ -39,7 +61,7 @@ __global__ __launch_bounds__(kThreads) void mfma_loop(int iters, float* __restri
   float s = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
-  sink[gid] = s;
+  store_through_lds<WPS>(lds, s, sink, gid);
 }
 
 // The same MFMA loop with realistic operands: each lane holds 8 different A
@@ -47,10 +69,11 @@ __global__ __launch_bounds__(kThreads) void mfma_loop(int iters, float* __restri
 // so the multiplier inputs change on every instruction as they do on real
 // tiles.  LDS = true: the A operand comes from a 32 KB LDS tile of the same
 // data instead (16 bytes per lane per MFMA, the score-MFMA access pattern).
-template <bool LDS>
+template <bool LDS, int WPS>
 __global__ __launch_bounds__(kThreads) void mfma_data_loop(const u32x4* __restrict__ src, int iters,
                                                           float* __restrict__ sink) {
-  __shared__ u32x4 tile[LDS ? 2048 : 1];
+  static_assert(reserve_bytes<WPS>() >= 2048 * 16, "the LDS tile lives in the reservation");
+  __shared__ u32x4 tile[reserve_bytes<WPS>() / 16];
   const int gid = blockIdx.x * kThreads + threadIdx.x;
   const int lane = threadIdx.x & 63;
   u32x4 a[8], b[8];
@@ -84,12 +107,18 @@ __global__ __launch_bounds__(kThreads) void mfma_data_loop(const u32x4* __restri
                                                     __builtin_bit_cast(bf16x8, b[i + 2]), c2, 0, 0, 0);
       c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x3),
                                                     __builtin_bit_cast(bf16x8, b[i + 3]), c3, 0, 0, 0);
+      // Register operands: keep the loop's scalar bookkeeping out from between
+      // the MFMAs.  With two or three waves per SIMD, a scalar instruction
+      // between them measurably lowers the rate this loop sustains, below the
+      // board's power limit, and the probe is meant to show the matrix cores'
+      // own ceiling.
+      if (!LDS) __builtin_amdgcn_sched_barrier(0);
     }
   }
   float s = 0.f;
 #pragma unroll
   for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
-  sink[gid] = s;
+  store_through_lds<WPS>(tile, s, sink, gid);
 }
 
 // Eight independent chains x <- 2^(-x) of v_exp_f32 per lane (the negation is
@@ -141,30 +170,47 @@ __global__ __launch_bounds__(kThreads) void atomic_loop(float* __restrict__ dst,
 
 int status(hipError_t e) { return e == hipSuccess ? 0 : -6; }
 
+template <bool LDS>
+hipError_t launch_mfma_data(int waves_per_simd, int workgroups, const u32x4* src, int iters, float* sink,
+                            hipStream_t stream) {
+  if (waves_per_simd == 1)
+    hipLaunchKernelGGL((mfma_data_loop<LDS, 1>), dim3(workgroups), dim3(kThreads), 0, stream, src, iters, sink);
+  else if (waves_per_simd == 2)
+    hipLaunchKernelGGL((mfma_data_loop<LDS, 2>), dim3(workgroups), dim3(kThreads), 0, stream, src, iters, sink);
+  else
+    hipLaunchKernelGGL((mfma_data_loop<LDS, 3>), dim3(workgroups), dim3(kThreads), 0, stream, src, iters, sink);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 extern "C" {
 
 int streamkl_probe_threads(void) { return kThreads; }
 
-int streamkl_probe_mfma(int workgroups, int iters, float* sink, size_t sink_floats, hipStream_t stream) {
-  if (workgroups < 1 || iters < 1 || !sink || sink_floats < (size_t)workgroups * kThreads) return -1;
-  hipLaunchKernelGGL(mfma_loop, dim3(workgroups), dim3(kThreads), 0, stream, iters, sink);
+int streamkl_probe_mfma(int waves_per_simd, int workgroups, int iters, float* sink, size_t sink_floats,
+                        hipStream_t stream) {
+  if (waves_per_simd < 1 || waves_per_simd > 3 || workgroups < 1 || iters < 1 || !sink ||
+      sink_floats < (size_t)workgroups * kThreads)
+    return -1;
+  if (waves_per_simd == 1)
+    hipLaunchKernelGGL(mfma_loop<1>, dim3(workgroups), dim3(kThreads), 0, stream, iters, sink);
+  else if (waves_per_simd == 2)
+    hipLaunchKernelGGL(mfma_loop<2>, dim3(workgroups), dim3(kThreads), 0, stream, iters, sink);
+  else
+    hipLaunchKernelGGL(mfma_loop<3>, dim3(workgroups), dim3(kThreads), 0, stream, iters, sink);
   return status(hipGetLastError());
 }
 
-int streamkl_probe_mfma_data(const void* src, size_t src_bytes, int from_lds, int workgroups, int iters, float* sink,
-                             size_t sink_floats, hipStream_t stream) {
-  if (!src || workgroups < 1 || iters < 1 || !sink || sink_floats < (size_t)workgroups * kThreads ||
-      ((uintptr_t)src & 15) != 0 || src_bytes < (size_t)workgroups * kThreads * 256)
+int streamkl_probe_mfma_data(const void* src, size_t src_bytes, int from_lds, int waves_per_simd, int workgroups,
+                             int iters, float* sink, size_t sink_floats, hipStream_t stream) {
+  if (!src || waves_per_simd < 1 || waves_per_simd > 3 || workgroups < 1 || iters < 1 || !sink ||
+      sink_floats < (size_t)workgroups * kThreads || ((uintptr_t)src & 15) != 0 ||
+      src_bytes < (size_t)workgroups * kThreads * 256)
     return -1;
-  if (from_lds)
-    hipLaunchKernelGGL(mfma_data_loop<true>, dim3(workgroups), dim3(kThreads), 0, stream, (const u32x4*)src, iters,
-                       sink);
-  else
-    hipLaunchKernelGGL(mfma_data_loop<false>, dim3(workgroups), dim3(kThreads), 0, stream, (const u32x4*)src, iters,
-                       sink);
-  return status(hipGetLastError());
+  const u32x4* s = (const u32x4*)src;
+  return status(from_lds ? launch_mfma_data<true>(waves_per_simd, workgroups, s, iters, sink, stream)
+                         : launch_mfma_data<false>(waves_per_simd, workgroups, s, iters, sink, stream));
 }
 
 int streamkl_probe_exp(int workgroups, int iters, float* sink, size_t sink_floats, hipStream_t stream) {

@@ -41,7 +41,11 @@ def test_probe_library_exports_and_validates():
     # invalid arguments are refused before any launch
     t = lib.streamkl_probe_threads()
     assert t == 256
-    assert lib.streamkl_probe_mfma(4, 10, FAKE, 4 * t - 1, None) == -1
+    assert lib.streamkl_probe_mfma(1, 4, 10, FAKE, 4 * t - 1, None) == -1
+    assert lib.streamkl_probe_mfma(4, 4, 10, FAKE, 4 * t, None) == -1              # 1 to 3 waves per SIMD
+    assert lib.streamkl_probe_mfma(0, 4, 10, FAKE, 4 * t, None) == -1
+    assert lib.streamkl_probe_mfma_data(FAKE, 4 * t * 256, 0, 4, 4, 10, FAKE, 4 * t, None) == -1
+    assert lib.streamkl_probe_mfma_data(FAKE, 4 * t * 256 - 16, 1, 2, 4, 10, FAKE, 4 * t, None) == -1
     assert lib.streamkl_probe_exp(0, 10, FAKE, 4 * t, None) == -1
     assert lib.streamkl_probe_read(FAKE, 100, 4, FAKE, 4 * t * 4, None) == -1      # not a multiple of 16
     assert lib.streamkl_probe_read(FAKE + 4, 64, 4, FAKE, 4 * t * 4, None) == -1   # misaligned
