@@ -5,16 +5,18 @@ configuration the benchmark times.
   forward on every row of heads 0 and 31 and on sampled rows of every other
   head (first and last rows, rows around query-tile boundaries, seeded random
   rows); both backward settings through the dK-only and dQ-only launches: dQ
-  on sampled rows of heads 0 and 31, dK on sampled keys of head 0 (from the
-  oracle's own per-row statistics of that head), and on every head the
-  identities sum_j dK_j = 0 and sum_i q_i . dQ_i = sum_j k_j . dK_j; the
+  on sampled rows of heads 0 and 31 and on a few rows of every other head
+  (single-setting and both-settings kernels), dK on sampled keys of head 0
+  (from the oracle's own per-row statistics of that head), and on every head
+  the identities sum_j dK_j = 0 and sum_i q_i . dQ_i = sum_j k_j . dK_j; the
   both-settings launches (the benchmark's) against those, element by element;
   and complete 128-key dK blocks and 128-query dQ blocks (first, middle,
   last) of heads 0 and 31 against the oracle, for both kernel families.
 * 512K-key decode (32 heads, one query): split-K with the automatic split count
   and with explicit counts, and the single-pass kernel, all heads.
 * 128K non-causal (32 heads): forward on sampled rows of every head; Setting 2
-  dQ on sampled rows of heads 0 and 31, dK on sampled keys of head 0, the
+  dQ on sampled rows of heads 0 and 31 and a few rows of every other head,
+  dK on sampled keys of head 0, the
   identities on every head, and complete 128-key dK and 128-query dQ blocks
   (first, middle, last) of heads 0 and 31.
 
@@ -111,12 +113,28 @@ def causal64k():
     state0 = _oracle_forward(a0, w, np.arange(w.n_q))
     a31 = head64(w, w.heads - 1)
     state31 = _oracle_forward(a31, w, np.arange(w.n_q))
-    log("causal64k: oracle heads 0 and 31 done")
-    return w, dev, (kl, l1, l2), grads, a0, state0, {0: (a0, state0), w.heads - 1: (a31, state31)}
+    log("causal64k: oracle heads 0 and 31 done; sampled rows of the other heads")
+    others = dict(pmap(lambda h: (h, _other_head(w, h)), range(1, w.heads - 1)))
+    log("causal64k: oracle rows of every head done")
+    return w, dev, (kl, l1, l2), grads, a0, state0, {0: (a0, state0), w.heads - 1: (a31, state31)}, others
+
+
+def _other_head(w, h):
+    """Oracle values on sampled rows of one head (inputs generated once): the
+    forward on first/last rows, rows around query-tile boundaries and random
+    rows; dQ of both settings on a few rows (each needs only its own row's
+    softmax)."""
+    a = head64(w, h)
+    rng = np.random.default_rng([21, h])
+    rows = _sample_rows(w.n_q, rng, edge=64, boundaries=8, random=64)
+    fwd = oracle.forward_head(*a, w.scale, w.causal, rows)
+    dq_rows = np.unique(np.concatenate([[0, 127, 128, w.n_q - 1], rng.integers(0, w.n_q, 4)]))
+    dq = {s: oracle.dq_rows(s, *a, w.scale, w.causal, dq_rows) for s in (1, 2)}
+    return rows, fwd, dq_rows, dq
 
 
 def test_causal64k_forward(causal64k):
-    w, dev, (kl, l1, l2), _, _, state0, full = causal64k
+    w, dev, (kl, l1, l2), _, _, state0, full, others = causal64k
     kl, l1, l2 = [t.cpu().numpy() for t in (kl, l1, l2)]
     rkl, rl1, rl2 = state0
     compare(l1[0], rl1, "bf16", "h0 lse1")
@@ -127,11 +145,7 @@ def test_causal64k_forward(causal64k):
     compare(l1[h], rl1, "bf16", f"h{h} lse1")
     compare(l2[h], rl2, "bf16", f"h{h} lse2")
     compare(kl[h], rkl, "bf16", f"h{h} kl")
-    rng = np.random.default_rng(21)
-    for h in range(1, w.heads - 1):
-        rows = _sample_rows(w.n_q, rng, edge=64, boundaries=8, random=64)
-        a = head64(w, h)
-        rkl, rl1, rl2 = _oracle_forward(a, w, rows)
+    for h, (rows, (rkl, rl1, rl2), _, _) in others.items():
         compare(l1[h, rows], rl1, "bf16", f"h{h} lse1")
         compare(l2[h, rows], rl2, "bf16", f"h{h} lse2")
         compare(kl[h, rows], rkl, "bf16", f"h{h} kl")
@@ -140,7 +154,7 @@ def test_causal64k_forward(causal64k):
 
 @pytest.mark.parametrize("setting", [1, 2])
 def test_causal64k_backward(causal64k, setting):
-    w, dev, _, grads, a0, state0, _ = causal64k
+    w, dev, _, grads, a0, state0, _, others = causal64k
     dq, dk = grads[setting]
     # the both-settings launches: the same per-pair arithmetic and accumulation
     # order as the single-setting kernels
@@ -158,6 +172,14 @@ def test_causal64k_backward(causal64k, setting):
     keys = _sample_rows(w.n_k, rng, edge=16, boundaries=4, random=32)
     rdk = _oracle_dk(a0, w, setting, keys, state0)
     compare(dk[0, keys].cpu().numpy(), rdk, "bf16", f"setting {setting} h0 dk")
+    # every other head: a few dQ rows against the oracle (each needs only its own
+    # row's softmax), for both kernel families; with the identity
+    # sum q.dQ = sum k.dK above this also fixes each head's dK scale
+    dqb = grads[f"both{setting}"][0]
+    for h, (_, _, rows, rdqs) in others.items():
+        rdq = rdqs[setting]
+        compare(dq[h, rows].cpu().numpy(), rdq, "bf16", f"setting {setting} h{h} dq rows")
+        compare(dqb[h, rows].cpu().numpy(), rdq, "bf16", f"both-settings {setting} h{h} dq rows")
     log(f"causal64k setting {setting}: checked")
 
 
@@ -173,7 +195,7 @@ def test_causal64k_full_blocks(causal64k, setting):
     (first, mid-sequence on the causal diagonal, last) on heads 0 and 31,
     against the oracle, for the single-setting kernels and for the
     both-settings kernels the benchmark times."""
-    w, dev, _, grads, _, _, full = causal64k
+    w, dev, _, grads, _, _, full, _ = causal64k
     for h, (a, state) in full.items():
         for blk in _full_blocks(w.n_k):
             rdk = _oracle_dk(a, w, setting, blk, state)
@@ -226,14 +248,23 @@ def test_noncausal128k_forward_setting2():
     log("noncausal128k: GPU done")
     _identities(q1, k1, dq, dk, "noncausal128k setting 2")
     kl, l1, l2 = [t.cpu().numpy() for t in (kl, l1, l2)]
-    rng = np.random.default_rng(41)
-    for h in range(w.heads):
-        rows = _sample_rows(w.n_q, rng, edge=16, boundaries=4, random=16)
-        rkl, rl1, rl2 = _oracle_forward(head64(w, h), w, rows)
+
+    def per_head(h):
+        # each head's inputs generated once: forward rows and a few Setting 2 dQ rows
+        a = head64(w, h)
+        r = np.random.default_rng([41, h])
+        rows = _sample_rows(w.n_q, r, edge=16, boundaries=4, random=16)
+        few = np.unique(np.concatenate([[0, w.n_q - 1], r.integers(0, w.n_q, 4)]))
+        return h, rows, oracle.forward_head(*a, w.scale, w.causal, rows), few, oracle.dq_rows(2, *a, w.scale,
+                                                                                              w.causal, few)
+
+    for h, rows, (rkl, rl1, rl2), few, rdq in pmap(per_head, range(w.heads)):
         compare(l1[h, rows], rl1, "bf16", f"h{h} lse1")
         compare(l2[h, rows], rl2, "bf16", f"h{h} lse2")
         compare(kl[h, rows], rkl, "bf16", f"h{h} kl")
-    log("noncausal128k: forward rows checked; oracle head 0 (all rows)")
+        compare(dq[h, few].cpu().numpy(), rdq, "bf16", f"h{h} dq1 rows")
+    log("noncausal128k: forward rows and dQ rows of every head checked; oracle head 0 (all rows)")
+    rng = np.random.default_rng(41)
     a0 = head64(w, 0)
     rows = _sample_rows(w.n_q, rng, edge=16, boundaries=4, random=48)
     for h in (0, w.heads - 1):
