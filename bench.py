@@ -100,12 +100,15 @@ def upload(w: W.Workload, threads: int):
 
 
 def kernel_source_hash() -> str:
-    """Hash of the device code (the .hip and .hpp files); host-only files such
-    as the C ABI's argument checks do not change what a kernel moves."""
+    """Hash of the attention-KL library's device code (its .hip sources and
+    the headers beside them).  Host-only files such as the C ABI's argument
+    checks, and the calibration probes (a library of their own), do not change
+    what a kernel moves."""
+    from streaming_kl_divergence_amd.build import SOURCES
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "streaming_kl_divergence_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp")):
+        if (f.endswith(".hip") and f in SOURCES) or f.endswith(".hpp"):
             with open(os.path.join(csrc, f), "rb") as fh:
                 h.update(fh.read())
     return h.hexdigest()[:16]
