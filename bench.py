@@ -642,7 +642,19 @@ def calibrate_mode(reps: int = 5, mfma_seconds: float = 3.0):
     wave_insts = wg * 4 * iters * 8
     out["exp_wave_insts_per_s"] = wave_insts / (ms * 1e-3)
     out["exp_cycles_per_wave_inst_per_simd"] = round(4 * cus * clk * (ms * 1e-3) / wave_insts, 2)
-    del sink
+    # exp beside FMA: two waves per SIMD, both exp, both FMA, or one of each
+    # (equal instructions per wave); if the mixed run takes the mean of the two
+    # pure runs the instructions take turns, if half the slower one they overlap
+    mix_sink = torch.empty(cus * 512, device="cuda")
+    mix = {}
+    for name, mode in (("exp", 0), ("fma", 1), ("mixed", 2)):
+        mix[name] = run(lambda: P.streamkl_probe_exp_fma(mode, cus, 100000, mix_sink.data_ptr(), mix_sink.numel(), s))
+        out[f"exp_fma_{name}_ms"] = round(mix[name], 3)
+    simd_insts = 2 * 100000 * 8                       # per SIMD: two waves x trips x 8
+    out["fma_cycles_per_wave_inst_per_simd"] = round(clk * mix["fma"] * 1e-3 / simd_insts, 2)
+    out["exp_fma_mixed_over_turns"] = round(mix["mixed"] / ((mix["exp"] + mix["fma"]) / 2), 3)
+    out["exp_fma_mixed_over_overlap"] = round(mix["mixed"] / (max(mix["exp"], mix["fma"]) / 2), 3)
+    del sink, mix_sink
     # HBM read: 8 GiB, 8 workgroups per CU
     nbytes = 8 << 30
     src = torch.empty(nbytes // 4, device="cuda", dtype=torch.float32).fill_(1.0)

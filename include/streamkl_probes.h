@@ -12,6 +12,8 @@
  *                          changing on every instruction), from registers or
  *                          with the A operand from LDS;
  *   streamkl_probe_exp     v_exp_f32 issue rate (8 per lane per loop trip);
+ *   streamkl_probe_exp_fma whether exp and FMA from two waves of a SIMD
+ *                          issue in the same cycles;
  *   streamkl_probe_read    HBM read rate (16-byte loads, grid-stride);
  *   streamkl_probe_atomic  fp32 atomic-add rate (4-byte payload per add).
  * They compute nothing of the method itself.
@@ -49,6 +51,14 @@ int streamkl_probe_mfma_data(const void* src, size_t src_bytes, int from_lds, in
 /* workgroups x 256 threads, each `iters` trips of 8 independent v_exp_f32.
  * sink: >= workgroups * threads floats. */
 int streamkl_probe_exp(int workgroups, int iters, float* sink, size_t sink_floats, hipStream_t stream);
+
+/* Whether v_exp_f32 and v_fma_f32 from two waves on one SIMD issue together:
+ * workgroups x 8 waves (512 threads), one workgroup per compute unit, each wave
+ * `iters` trips of 8 independent chains.  mode 0: all waves exp; 1: all FMA;
+ * 2: four waves exp and four FMA (one of each per SIMD).
+ * sink: >= workgroups * 512 floats. */
+int streamkl_probe_exp_fma(int mode, int workgroups, int iters, float* sink, size_t sink_floats,
+                           hipStream_t stream);
 
 /* Reads `bytes` (a multiple of 16) of src (16-byte aligned) once.
  * sink: >= workgroups * threads * 4 bytes. */

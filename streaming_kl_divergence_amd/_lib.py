@@ -42,12 +42,14 @@ _lib = None
 
 PROBES_PATH = os.path.join(PKG, "libstreamkl_probes.so")
 PROBE_EXPORTS = ("streamkl_probe_threads", "streamkl_probe_mfma", "streamkl_probe_mfma_data", "streamkl_probe_exp",
+                 "streamkl_probe_exp_fma",
                  "streamkl_probe_read", "streamkl_probe_atomic")
 _PROBE_SIGS = {
     "streamkl_probe_threads": (_I, []),
     "streamkl_probe_mfma": (_I, [_I, _I, _I, _P, _Z, _P]),
     "streamkl_probe_mfma_data": (_I, [_P, _Z, _I, _I, _I, _I, _P, _Z, _P]),
     "streamkl_probe_exp": (_I, [_I, _I, _P, _Z, _P]),
+    "streamkl_probe_exp_fma": (_I, [_I, _I, _I, _P, _Z, _P]),
     "streamkl_probe_read": (_I, [_P, _Z, _I, _P, _Z, _P]),
     "streamkl_probe_atomic": (_I, [_P, _Z, _I, _I, _P]),
 }

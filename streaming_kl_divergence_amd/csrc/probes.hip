@@ -139,6 +139,46 @@ __global__ __launch_bounds__(kThreads) void exp_loop(int iters, float* __restric
   sink[gid] = s;
 }
 
+// Eight waves per workgroup, one workgroup per CU (LDS reservation), so each
+// SIMD holds two waves (waves w and w + 4 of a workgroup share a SIMD as the
+// dispatcher deals them out).  MODE 0: every wave runs eight independent
+// v_exp_f32 chains; MODE 1: eight independent v_fma_f32 chains; MODE 2: waves
+// 0-3 run the exp chains and waves 4-7 the FMA chains, so each SIMD holds one
+// of each.  Equal instruction counts per wave in every mode: comparing the
+// three times shows whether a transcendental from one wave and an FMA from
+// another issue in the same cycles or take turns.
+constexpr int kMixThreads = 512;
+
+template <int MODE>
+__global__ __launch_bounds__(kMixThreads) void exp_fma_loop(int iters, float* __restrict__ sink) {
+  __shared__ float lds[96 * 1024 / 4];
+  const int gid = blockIdx.x * kMixThreads + threadIdx.x;
+  const int wave = threadIdx.x / 64;
+  const bool exp_wave = MODE == 0 || (MODE == 2 && wave < 4);
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = 0.01f * (float)((threadIdx.x + j) & 15);
+  if (exp_wave) {
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = __builtin_amdgcn_exp2f(-x[j]);
+    }
+  } else {
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = __builtin_fmaf(x[j], 0.999f, 0.001f);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += x[j];
+  // through the reserved LDS, so the reservation is part of the kernel
+  __syncthreads();
+  lds[threadIdx.x] = s;
+  __syncthreads();
+  sink[gid] = lds[(threadIdx.x + 1) % kMixThreads];
+}
+
 // Grid-stride read of n16 16-byte words, four independent loads in flight
 // per thread; a per-thread XOR of what was read goes to sink[gid].
 __global__ __launch_bounds__(kThreads) void read_loop(const uint4* __restrict__ src, size_t n16,
@@ -216,6 +256,19 @@ int streamkl_probe_mfma_data(const void* src, size_t src_bytes, int from_lds, in
 int streamkl_probe_exp(int workgroups, int iters, float* sink, size_t sink_floats, hipStream_t stream) {
   if (workgroups < 1 || iters < 1 || !sink || sink_floats < (size_t)workgroups * kThreads) return -1;
   hipLaunchKernelGGL(exp_loop, dim3(workgroups), dim3(kThreads), 0, stream, iters, sink);
+  return status(hipGetLastError());
+}
+
+int streamkl_probe_exp_fma(int mode, int workgroups, int iters, float* sink, size_t sink_floats,
+                           hipStream_t stream) {
+  if (mode < 0 || mode > 2 || workgroups < 1 || iters < 1 || !sink || sink_floats < (size_t)workgroups * kMixThreads)
+    return -1;
+  if (mode == 0)
+    hipLaunchKernelGGL(exp_fma_loop<0>, dim3(workgroups), dim3(kMixThreads), 0, stream, iters, sink);
+  else if (mode == 1)
+    hipLaunchKernelGGL(exp_fma_loop<1>, dim3(workgroups), dim3(kMixThreads), 0, stream, iters, sink);
+  else
+    hipLaunchKernelGGL(exp_fma_loop<2>, dim3(workgroups), dim3(kMixThreads), 0, stream, iters, sink);
   return status(hipGetLastError());
 }
 
