@@ -658,15 +658,16 @@ def calibrate_mode(reps: int = 5, mfma_seconds: float = 3.0):
     # HBM read: 8 GiB, 8 workgroups per CU
     nbytes = 8 << 30
     src = torch.empty(nbytes // 4, device="cuda", dtype=torch.float32).fill_(1.0)
-    best = 0.0
-    for wgr in (4 * cus, 8 * cus, 16 * cus, 32 * cus):
-        snk = torch.empty(wgr * T, device="cuda", dtype=torch.int32)
-        ms = run(lambda: P.streamkl_probe_read(src.data_ptr(), nbytes, wgr, snk.data_ptr(), snk.numel() * 4, s))
-        out[f"read_gbs_{wgr}wg"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
-        best = max(best, nbytes / (ms * 1e-3) / 1e9)
-        del snk
-    out["read_gbs_best"] = round(best, 1)
-    out["read_frac_of_hbm_peak"] = round(best / PEAK_HBM_GBS, 4)
+    for nt, tag in ((0, ""), (1, "nt_")):
+        best = 0.0
+        for wgr in (4 * cus, 8 * cus, 16 * cus, 32 * cus):
+            snk = torch.empty(wgr * T, device="cuda", dtype=torch.int32)
+            ms = run(lambda: P.streamkl_probe_read(src.data_ptr(), nbytes, nt, wgr, snk.data_ptr(), snk.numel() * 4, s))
+            out[f"read_{tag}gbs_{wgr}wg"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+            best = max(best, nbytes / (ms * 1e-3) / 1e9)
+            del snk
+        out[f"read_{tag}gbs_best"] = round(best, 1)
+        out[f"read_{tag}frac_of_hbm_peak"] = round(best / PEAK_HBM_GBS, 4)
     del src
     # fp32 atomics: 1 GiB (the size of one 64K-causal dQ) and 2 MiB (fits one XCD's L2)
     for name, n, r in (("1GiB", (1 << 30) // 4, 2), ("2MiB", (2 << 20) // 4, 512)):

@@ -14,7 +14,8 @@
  *   streamkl_probe_exp     v_exp_f32 issue rate (8 per lane per loop trip);
  *   streamkl_probe_exp_fma whether exp and FMA from two waves of a SIMD
  *                          issue in the same cycles;
- *   streamkl_probe_read    HBM read rate (16-byte loads, grid-stride);
+ *   streamkl_probe_read    HBM read rate (16-byte loads, grid-stride, with or
+ *                          without the non-temporal cache policy);
  *   streamkl_probe_atomic  fp32 atomic-add rate (4-byte payload per add).
  * They compute nothing of the method itself.
  *
@@ -60,10 +61,11 @@ int streamkl_probe_exp(int workgroups, int iters, float* sink, size_t sink_float
 int streamkl_probe_exp_fma(int mode, int workgroups, int iters, float* sink, size_t sink_floats,
                            hipStream_t stream);
 
-/* Reads `bytes` (a multiple of 16) of src (16-byte aligned) once.
+/* Reads `bytes` (a multiple of 16) of src (16-byte aligned) once; nontemporal
+ * != 0 marks the loads non-temporal (the nt cache policy, for data read once).
  * sink: >= workgroups * threads * 4 bytes. */
-int streamkl_probe_read(const void* src, size_t bytes, int workgroups, void* sink, size_t sink_bytes,
-                        hipStream_t stream);
+int streamkl_probe_read(const void* src, size_t bytes, int nontemporal, int workgroups, void* sink,
+                        size_t sink_bytes, hipStream_t stream);
 
 /* Adds 1.0f to each of dst[0 .. n_floats) `reps` times with fp32 atomics. */
 int streamkl_probe_atomic(float* dst, size_t n_floats, int workgroups, int reps, hipStream_t stream);

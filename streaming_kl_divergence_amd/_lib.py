@@ -50,7 +50,7 @@ _PROBE_SIGS = {
     "streamkl_probe_mfma_data": (_I, [_P, _Z, _I, _I, _I, _I, _P, _Z, _P]),
     "streamkl_probe_exp": (_I, [_I, _I, _P, _Z, _P]),
     "streamkl_probe_exp_fma": (_I, [_I, _I, _I, _P, _Z, _P]),
-    "streamkl_probe_read": (_I, [_P, _Z, _I, _P, _Z, _P]),
+    "streamkl_probe_read": (_I, [_P, _Z, _I, _I, _P, _Z, _P]),
     "streamkl_probe_atomic": (_I, [_P, _Z, _I, _I, _P]),
 }
 _probes = None

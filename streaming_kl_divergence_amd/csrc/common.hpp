@@ -127,21 +127,33 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // the DMA itself is ordered by wait_async_loads() and a barrier before any
 // wave reads the tile.  SALU writes to M0 need one wait state before an LDS
 // DMA, hence the s_nop.
+// NT marks the load non-temporal (the nt cache-policy bit): for data that no
+// other workgroup will read again, HBM streams it faster.
+template <bool NT = false>
 __device__ __forceinline__ void lds_dma_16(const void* src, uint32_t lds_base) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(src), "s"(lds_base)
-      : "memory", "m0");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off nt"
+        :
+        : "v"(src), "s"(lds_base)
+        : "memory", "m0");
+  else
+    asm volatile(
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, off"
+        :
+        : "v"(src), "s"(lds_base)
+        : "memory", "m0");
 }
 
 // Issue the asynchronous copy of a [BK, D] tile (rows key0 .. key0+BK-1 of the
 // head whose row 0 is at `g`) into LDS with the swizzled layout.  Rows past
 // n_rows are clamped to the last row, so every load is in bounds; the caller
 // masks those rows out.  Every lane of all NW waves takes part.
-template <typename T, int D, int BK, int NW>
+template <typename T, int D, int BK, int NW, bool NT = false>
 __device__ __forceinline__ void issue_tile_async(const char* __restrict__ g, int key0, int n_rows,
                                                  SKL_LDS char* tile, int tid, int wave) {
   using G = Geom<T, D>;
@@ -157,7 +169,7 @@ __device__ __forceinline__ void issue_tile_async(const char* __restrict__ g, int
     const int src_row = min(key0 + row, n_rows - 1);
     const char* src = g + (size_t)src_row * G::kRowBytes + c * 16;
     // lane i of this wave lands at base + 16 * i
-    lds_dma_16(src, __builtin_amdgcn_readfirstlane(
+    lds_dma_16<NT>(src, __builtin_amdgcn_readfirstlane(
                         (uint32_t)(uintptr_t)(tile + (i * NW * 64 + wave * 64) * 16)));
   }
 }
@@ -165,6 +177,7 @@ __device__ __forceinline__ void issue_tile_async(const char* __restrict__ g, int
 // The same copy in scalar-base form: a wave-uniform 64-bit base (SGPRs) plus a
 // 32-bit per-lane byte offset, so a tile that needs no clamping costs no
 // per-lane 64-bit address arithmetic.
+template <bool NT = false>
 __device__ __forceinline__ void lds_dma_16_sbase(const char* base, uint32_t voff, uint32_t lds_base) {
   // the base is wave-uniform by construction; make that visible to the
   // compiler so it stays in SGPRs
@@ -172,20 +185,30 @@ __device__ __forceinline__ void lds_dma_16_sbase(const char* base, uint32_t voff
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
   const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
   const char* sbase = (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(voff), "s"(sbase), "s"(lds_base)
-      : "memory", "m0");
+  if constexpr (NT)
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1 nt"
+        :
+        : "v"(voff), "s"(sbase), "s"(lds_base)
+        : "memory", "m0");
+  else
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(sbase), "s"(lds_base)
+        : "memory", "m0");
 }
 
 // Streams [BK, D] tiles of one head's rows into swizzled LDS tiles.  Each
 // lane's source offset inside a tile is fixed for the whole kernel, so it is
 // computed once; a full tile is then one scalar base per instruction.  A tile
-// that reaches past n_rows (the last one) takes the clamped path.
-template <typename T, int D, int BK, int NW>
+// that reaches past n_rows (the last one) takes the clamped path.  NT: the
+// loads are non-temporal (see lds_dma_16).
+template <typename T, int D, int BK, int NW, bool NT = false>
 struct TileStream {
   using G = Geom<T, D>;
   static constexpr int kSlots = BK * G::kChunks;
@@ -212,16 +235,16 @@ struct TileStream {
     for (int i = 0; i < kPer; ++i) {
       const uint32_t lb = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(tile + (i * NW * 64 + wave * 64) * 16));
       if constexpr (kPeriodic)
-        lds_dma_16_sbase(base + i * kRowsPerInst * G::kRowBytes, voff0, lb);
+        lds_dma_16_sbase<NT>(base + i * kRowsPerInst * G::kRowBytes, voff0, lb);
       else
-        lds_dma_16_sbase(base, lane_off(i, tid), lb);
+        lds_dma_16_sbase<NT>(base, lane_off(i, tid), lb);
     }
   }
 
   __device__ __forceinline__ void issue(const char* __restrict__ g, int key0, int n_rows, SKL_LDS char* tile,
                                         int tid, int wave) const {
     if (key0 + BK > n_rows) {
-      issue_tile_async<T, D, BK, NW>(g, key0, n_rows, tile, tid, wave);
+      issue_tile_async<T, D, BK, NW, NT>(g, key0, n_rows, tile, tid, wave);
       return;
     }
     issue_full(g, key0, tile, tid, wave);
@@ -234,8 +257,8 @@ struct TileStream {
                                          int n_rows, SKL_LDS char* tile1, SKL_LDS char* tile2, int tid,
                                          int wave) const {
     if (__builtin_expect(key0 + BK > n_rows, 0)) {
-      issue_tile_async<T, D, BK, NW>(g1, key0, n_rows, tile1, tid, wave);
-      issue_tile_async<T, D, BK, NW>(g2, key0, n_rows, tile2, tid, wave);
+      issue_tile_async<T, D, BK, NW, NT>(g1, key0, n_rows, tile1, tid, wave);
+      issue_tile_async<T, D, BK, NW, NT>(g2, key0, n_rows, tile2, tid, wave);
       return;
     }
     issue_full(g1, key0, tile1, tid, wave);

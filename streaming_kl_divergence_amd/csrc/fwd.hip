@@ -252,11 +252,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
 
   // Two waves per SIMD (223 VGPRs) overlap one wave's MFMAs with the other's VALU.
   f32x16 s1[NKB], s2[NKB];
-  TileStream<T, D, BK, NW> ts;
+  // A one-wave workgroup holds every query of its head (at most 32, the
+  // decode shape), so no other workgroup reads its keys: they are streamed
+  // with non-temporal loads.  Wider workgroups share each head's keys through
+  // the XCD's L2 and keep the default cache policy.
+  constexpr bool kStream = NW == 1;
+  TileStream<T, D, BK, NW, kStream> ts;
   ts.init(tid);
   if (ntiles > 0) {
-    issue_tile_async<T, D, BK, NW>(k1, kbeg, p.n_k, lds, tid, wave);
-    issue_tile_async<T, D, BK, NW>(k2, kbeg, p.n_k, lds + TILE, tid, wave);
+    issue_tile_async<T, D, BK, NW, kStream>(k1, kbeg, p.n_k, lds, tid, wave);
+    issue_tile_async<T, D, BK, NW, kStream>(k2, kbeg, p.n_k, lds + TILE, tid, wave);
   }
   // The last key this wave's first query may see: a tile holding a key past
   // it crosses the causal diagonal (wave-uniform).

@@ -180,20 +180,23 @@ __global__ __launch_bounds__(kMixThreads) void exp_fma_loop(int iters, float* __
 }
 
 // Grid-stride read of n16 16-byte words, four independent loads in flight
-// per thread; a per-thread XOR of what was read goes to sink[gid].
-__global__ __launch_bounds__(kThreads) void read_loop(const uint4* __restrict__ src, size_t n16,
+// per thread; a per-thread XOR of what was read goes to sink[gid].  NT: the
+// loads carry the non-temporal cache policy (data read once).
+template <bool NT>
+__global__ __launch_bounds__(kThreads) void read_loop(const u32x4* __restrict__ src, size_t n16,
                                                        uint32_t* __restrict__ sink) {
   const size_t gid = (size_t)blockIdx.x * kThreads + threadIdx.x;
   const size_t stride = (size_t)gridDim.x * kThreads;
+  auto load = [&](size_t i) { return NT ? __builtin_nontemporal_load(src + i) : src[i]; };
   uint32_t acc = 0;
   size_t i = gid;
   for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
+    const u32x4 v0 = load(i), v1 = load(i + stride), v2 = load(i + 2 * stride), v3 = load(i + 3 * stride);
     acc ^= (v0.x ^ v0.y ^ v0.z ^ v0.w) ^ (v1.x ^ v1.y ^ v1.z ^ v1.w) ^ (v2.x ^ v2.y ^ v2.z ^ v2.w) ^
            (v3.x ^ v3.y ^ v3.z ^ v3.w);
   }
   for (; i < n16; i += stride) {
-    const uint4 v = src[i];
+    const u32x4 v = load(i);
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   sink[gid] = acc;
@@ -272,13 +275,17 @@ int streamkl_probe_exp_fma(int mode, int workgroups, int iters, float* sink, siz
   return status(hipGetLastError());
 }
 
-int streamkl_probe_read(const void* src, size_t bytes, int workgroups, void* sink, size_t sink_bytes,
-                        hipStream_t stream) {
+int streamkl_probe_read(const void* src, size_t bytes, int nontemporal, int workgroups, void* sink,
+                        size_t sink_bytes, hipStream_t stream) {
   if (!src || !sink || workgroups < 1 || bytes % 16 != 0 || ((uintptr_t)src & 15) != 0 ||
       sink_bytes < (size_t)workgroups * kThreads * sizeof(uint32_t))
     return -1;
-  hipLaunchKernelGGL(read_loop, dim3(workgroups), dim3(kThreads), 0, stream, (const uint4*)src, bytes / 16,
-                     (uint32_t*)sink);
+  if (nontemporal)
+    hipLaunchKernelGGL(read_loop<true>, dim3(workgroups), dim3(kThreads), 0, stream, (const u32x4*)src, bytes / 16,
+                       (uint32_t*)sink);
+  else
+    hipLaunchKernelGGL(read_loop<false>, dim3(workgroups), dim3(kThreads), 0, stream, (const u32x4*)src, bytes / 16,
+                       (uint32_t*)sink);
   return status(hipGetLastError());
 }
 

@@ -49,8 +49,8 @@ def test_probe_library_exports_and_validates():
     assert lib.streamkl_probe_exp(0, 10, FAKE, 4 * t, None) == -1
     assert lib.streamkl_probe_exp_fma(3, 4, 10, FAKE, 4 * 512, None) == -1      # modes 0 to 2
     assert lib.streamkl_probe_exp_fma(2, 4, 10, FAKE, 4 * 512 - 1, None) == -1  # sink too small
-    assert lib.streamkl_probe_read(FAKE, 100, 4, FAKE, 4 * t * 4, None) == -1      # not a multiple of 16
-    assert lib.streamkl_probe_read(FAKE + 4, 64, 4, FAKE, 4 * t * 4, None) == -1   # misaligned
+    assert lib.streamkl_probe_read(FAKE, 100, 0, 4, FAKE, 4 * t * 4, None) == -1      # not a multiple of 16
+    assert lib.streamkl_probe_read(FAKE + 4, 64, 1, 4, FAKE, 4 * t * 4, None) == -1   # misaligned
     assert lib.streamkl_probe_atomic(None, 16, 4, 1, None) == -1
 
 
