@@ -173,7 +173,7 @@ __device__ __forceinline__ bool tile_fold_at_offsets(RowState& st, const f32x16*
   return true;
 }
 
-template <typename T, int D, int NW, bool SPLIT>
+template <typename T, int D, int NW, bool SPLIT, bool STREAM>
 __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   using G = Geom<T, D>;
   constexpr int BK = kFwdKeyTile;
@@ -252,16 +252,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
 
   // Two waves per SIMD (223 VGPRs) overlap one wave's MFMAs with the other's VALU.
   f32x16 s1[NKB], s2[NKB];
-  // A one-wave workgroup holds every query of its head (at most 32, the
-  // decode shape), so no other workgroup reads its keys: they are streamed
-  // with non-temporal loads.  Wider workgroups share each head's keys through
-  // the XCD's L2 and keep the default cache policy.
-  constexpr bool kStream = NW == 1;
-  TileStream<T, D, BK, NW, kStream> ts;
+  // STREAM: this workgroup holds every query of its head (one query block
+  // per head: decode and other short query sets), so no other workgroup reads
+  // its keys and they are streamed with non-temporal loads.  Otherwise the
+  // head's workgroups share its keys through the XCD's L2 and the loads keep
+  // the default cache policy.
+  TileStream<T, D, BK, NW, STREAM> ts;
   ts.init(tid);
   if (ntiles > 0) {
-    issue_tile_async<T, D, BK, NW, kStream>(k1, kbeg, p.n_k, lds, tid, wave);
-    issue_tile_async<T, D, BK, NW, kStream>(k2, kbeg, p.n_k, lds + TILE, tid, wave);
+    issue_tile_async<T, D, BK, NW, STREAM>(k1, kbeg, p.n_k, lds, tid, wave);
+    issue_tile_async<T, D, BK, NW, STREAM>(k2, kbeg, p.n_k, lds + TILE, tid, wave);
   }
   // The last key this wave's first query may see: a tile holding a key past
   // it crosses the causal diagonal (wave-uniform).
@@ -373,7 +373,14 @@ template <typename T, int D, int NW, bool SPLIT>
 static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
   const int nqb = (p.n_q + 32 * NW - 1) / (32 * NW);
   const long long blocks = SPLIT ? (long long)p.heads * nqb * p.splits : (long long)xcd_grid(p.heads * nqb);
-  hipLaunchKernelGGL((fwd_kernel<T, D, NW, SPLIT>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, p);
+  // one query block per head: every key byte is read by a single workgroup.
+  // One-wave workgroups are used only for such shapes (at most 32 queries).
+  if constexpr (NW == 1)
+    hipLaunchKernelGGL((fwd_kernel<T, D, 1, SPLIT, true>), dim3((unsigned)blocks), dim3(64), 0, stream, p);
+  else if (nqb == 1)
+    hipLaunchKernelGGL((fwd_kernel<T, D, NW, SPLIT, true>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_kernel<T, D, NW, SPLIT, false>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, p);
   return hipGetLastError();
 }
 
