@@ -114,6 +114,9 @@ int streamkl_fwd(const void* q1, const void* k1, const void* q2, const void* k2,
  * `workspace`, and a second kernel on the same stream merges the states and
  * writes kl, lse1, lse2 as streamkl_fwd does.  num_splits = 0 lets the
  * library choose (streamkl_splitk_auto); otherwise 1 <= num_splits <= 1024.
+ * A call whose grid would reach 2^31 workgroups (heads x query blocks x
+ * splits; a query block is 128 queries, or 32 when n_q <= 32) returns
+ * STREAMKL_ERR_SHAPE.
  * workspace: device memory of at least
  *   streamkl_workspace_bytes(0, n_q, n_k, heads, head_dim, num_splits, 0)
  * bytes, owned by the caller; its contents on entry are ignored.

@@ -16,6 +16,9 @@
 namespace {
 
 constexpr int kMaxSplits = 1024;
+// Largest split-K grid: the kernel indexes its (head, split, query block)
+// work items with 32-bit integers (and pads the grid to a multiple of 8).
+constexpr long long kMaxWorkgroups = (1LL << 31) - 64;
 
 // Experiment overrides and dispatch logging, read from the environment once per
 // process, at the first call that needs them:
@@ -262,6 +265,7 @@ int streamkl_fwd_splitk(const void* q1, const void* k1, const void* q2, const vo
   if (num_splits < 0 || num_splits > kMaxSplits) return lg.done(STREAMKL_ERR_UNSUPPORTED);
   size_t need = 0;
   const int splits = splitk_count(n_q, n_k, heads, head_dim, num_splits, &need);
+  if (fwd_workgroups(n_q, heads, splits) > kMaxWorkgroups) return lg.done(STREAMKL_ERR_SHAPE);
   lg.choose("splits=%d (%s) keys_per_split=%d workgroups=%lld workspace=%zu/%zu", splits,
             splits_source(num_splits), split_keys_for(n_k, splits), fwd_workgroups(n_q, heads, splits), need,
             workspace_bytes);
@@ -281,6 +285,7 @@ int streamkl_fwd_splitk_noalloc(const void* q1, const void* k1, const void* q2, 
   if (num_splits < 0 || num_splits > kMaxSplits) return lg.done(STREAMKL_ERR_UNSUPPORTED);
   size_t need = 0;
   const int splits = splitk_count(n_q, n_k, heads, head_dim, num_splits, &need);
+  if (fwd_workgroups(n_q, heads, splits) > kMaxWorkgroups) return lg.done(STREAMKL_ERR_SHAPE);
   lg.choose("splits=%d (%s) keys_per_split=%d workgroups=%lld scratch=%zu/%zu", splits, splits_source(num_splits),
             split_keys_for(n_k, splits), fwd_workgroups(n_q, heads, splits), need, skl::kNoAllocScratchBytes);
   if (need > skl::kNoAllocScratchBytes) return lg.done(STREAMKL_ERR_TOO_LARGE);

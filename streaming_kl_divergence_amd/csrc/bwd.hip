@@ -456,10 +456,15 @@ __global__ __launch_bounds__(256) void bwd_q_kernel(BwdParams p) {
   int bid = blockIdx.x;
   int head, split = 0;
   if (SPLIT) {
-    head = bid % p.heads;
-    bid /= p.heads;
-    split = bid % p.dq_splits;
-    bid /= p.dq_splits;
+    // work items (head, key range, query block), query block fastest, dealt
+    // to the XCDs in contiguous runs: the workgroups that share one key range
+    // run side by side on one XCD and stream its tiles through one L2
+    const int total = p.heads * p.dq_splits * nqb;
+    const int w = xcd_work_index(bid, total);
+    if (w >= total) return;
+    bid = w % nqb;
+    split = (w / nqb) % p.dq_splits;
+    head = w / (nqb * p.dq_splits);
   } else {
     const int w = xcd_work_index(bid, p.heads * nqb);
     if (w >= p.heads * nqb) return;
@@ -635,7 +640,7 @@ static hipError_t sep(const BwdParams& p, bool do_dk, bool do_dq, hipStream_t s)
   if (p.dq_splits > 1) {
     e = zero_fill(p.dq, (size_t)p.heads * p.n_q * D, s);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_q_kernel<T, D, SETTING, true, HAS_G>), dim3(p.heads * nqb * p.dq_splits), dim3(256), 0, s,
+    hipLaunchKernelGGL((bwd_q_kernel<T, D, SETTING, true, HAS_G>), dim3(xcd_grid(p.heads * nqb * p.dq_splits)), dim3(256), 0, s,
                        p);
   } else {
     hipLaunchKernelGGL((bwd_q_kernel<T, D, SETTING, false, HAS_G>), dim3(xcd_grid(p.heads * nqb)), dim3(256), 0, s, p);

@@ -193,10 +193,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   int bid = blockIdx.x;
   int head, split = 0;
   if (SPLIT) {
-    head = bid % p.heads;
-    bid /= p.heads;
-    split = bid % p.splits;
-    bid /= p.splits;
+    // work items (head, split, query block), query block fastest, dealt to
+    // the XCDs in contiguous runs: the workgroups that share one key range
+    // run side by side on one XCD and stream its tiles through one L2
+    const int total = p.heads * p.splits * nqb;
+    const int w = xcd_work_index(bid, total);
+    if (w >= total) return;
+    bid = w % nqb;
+    split = (w / nqb) % p.splits;
+    head = w / (nqb * p.splits);
   } else {
     const int w = xcd_work_index(bid, p.heads * nqb);
     if (w >= p.heads * nqb) return;
@@ -372,7 +377,7 @@ __global__ __launch_bounds__(256) void splitk_combine_kernel(FwdParams p) {
 template <typename T, int D, int NW, bool SPLIT>
 static hipError_t launch_one(const FwdParams& p, hipStream_t stream) {
   const int nqb = (p.n_q + 32 * NW - 1) / (32 * NW);
-  const long long blocks = SPLIT ? (long long)p.heads * nqb * p.splits : (long long)xcd_grid(p.heads * nqb);
+  const long long blocks = xcd_grid(SPLIT ? p.heads * nqb * p.splits : p.heads * nqb);
   // one query block per head: every key byte is read by a single workgroup.
   // One-wave workgroups are used only for such shapes (at most 32 queries).
   if constexpr (NW == 1)

@@ -90,6 +90,17 @@ def test_splitk_validation():
     assert lib.streamkl_workspace_bytes(1, 1, 4096, 2, 128, 0, 0) == 0
 
 
+def test_splitk_refuses_a_grid_beyond_32_bit_work_indices():
+    lib = L.lib()
+    # 2^30 queries of one head: 2^23 query blocks x 1024 splits = 2^33 workgroups
+    n = 1 << 30
+    args = [FAKE] * 4 + [n, n, 1, 128, 0, 0.1, L.BF16]
+    assert lib.streamkl_fwd_splitk(*args, 1024, FAKE, FAKE, FAKE, FAKE, 1 << 62, None) == L.ERR_SHAPE
+    assert lib.streamkl_fwd_splitk_noalloc(*args, 1024, FAKE, FAKE, FAKE, None) == L.ERR_SHAPE
+    # the same head with 255 splits stays below 2^31 workgroups and reaches the workspace check
+    assert lib.streamkl_fwd_splitk(*args, 255, FAKE, FAKE, FAKE, FAKE, 16, None) == L.ERR_WORKSPACE
+
+
 def test_noalloc_splitk_refuses_more_than_its_scratch():
     """streamkl_fwd_splitk_noalloc validates like streamkl_fwd_splitk and
     refuses a problem whose partial states exceed its fixed 8 MiB scratch,
