@@ -56,6 +56,8 @@ BWD_EDGE = [
     (2, 400, 900, 128, "bf16", True, 4.0),
     (1, 128, 128, 128, "bf16", True, 1.0),
     (2, 200, 300, 128, "bf16", True, 0.0),    # scale 0: uniform rows, zero gradients
+    (2, 300, 3000, 128, "bf16", True, 1.0),   # few query blocks, long keys: dQ over 3 key ranges, causal
+    (3, 257, 4100, 64, "bf16", False, 1.0),   # dQ over 5 key ranges, ragged tail
 ]
 
 
