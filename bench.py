@@ -39,9 +39,16 @@ Usage:
       also runs one plain 1 GiB device copy first, so that a rocprofv3 --pmc
       run sees FETCH_SIZE / WRITE_SIZE of a copy of known size.
   python bench.py --calibrate
-      the calibration probes (libstreamkl_probes.so): a pure bf16 MFMA loop,
-      the v_exp_f32 issue rate, a plain 8 GiB HBM read and fp32 atomic adds,
-      the measured ceilings beside the published peaks.
+      the calibration probes (libstreamkl_probes.so): bf16 MFMA loops at 1-3
+      waves per SIMD with constant and realistic operands (with board watts),
+      the v_exp_f32 issue rate and whether it overlaps FMAs, plain 8 GiB HBM
+      reads (default and non-temporal) and fp32 atomic adds: the measured
+      ceilings beside the published peaks.
+  python -m streaming_kl_divergence_amd.build --rev REV
+  python bench.py --ab LIB_A,LIB_B [--workload NAME] [--ab-calls fwd,dk_both,...]
+      two builds of the library (the second, say, from an earlier revision)
+      timed against each other in one process on the same inputs, launches
+      alternating; medians, ratios and whether the outputs are bitwise equal.
   python bench.py --power
       board power (the GPU's hwmon sensor) while each kernel of the 64K
       causal step runs back to back, beside idle power and MFMA probes with
@@ -582,6 +589,102 @@ def power_mode(seconds: float = 5.0):
     ps.stop()
 
 
+def ab_mode(libs: list[str], workload: str, calls: list[str] | None = None, rounds: int = 8, per: int = 5):
+    """Two or more builds of libstreamkl.so (for instance one built with
+    `python -m streaming_kl_divergence_amd.build --rev REV`) timed against each
+    other in one process on the same inputs: for every call, `rounds` rounds in
+    which each build runs one untimed and `per` timed launches (HIP events on
+    the launching stream), the order of the builds alternating between rounds;
+    the median per build, its ratio to the first build, and whether the outputs
+    are bitwise equal (else their largest relative difference).  One JSON line
+    per call.  Box-to-box differences cancel; on one box two builds of the same
+    code have differed by up to a few percent, so a smaller difference is not a
+    result."""
+    import ctypes
+    import torch
+    from streaming_kl_divergence_amd import _lib
+    w = W.WORKLOADS[workload]
+    default = {"causal64k": ["fwd", "dk_both", "dq_both"], "decode512k": ["splitk"], "smallq128k": ["splitk", "dq2"]}
+    calls = calls or default.get(workload, ["fwd"])
+    loaded = []
+    for path in libs:
+        l = ctypes.CDLL(os.path.abspath(path), mode=ctypes.RTLD_LOCAL)
+        for name, (res, args) in _lib._SIGS.items():
+            f = getattr(l, name, None)
+            if f is not None:
+                f.restype, f.argtypes = res, args
+        loaded.append(l)
+    q1, k1, q2, k2 = upload(w, min(16, os.cpu_count() or 1))
+    H, NQ, NK, d = w.heads, w.n_q, w.n_k, w.head_dim
+    dt = _lib.BF16 if w.dtype == "bf16" else _lib.FP32
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+    base = (q1.data_ptr(), k1.data_ptr(), q2.data_ptr(), k2.data_ptr(), NQ, NK, H, d, int(w.causal), w.scale, dt)
+    f32 = dict(device="cuda", dtype=torch.float32)
+    state = [torch.empty(H, NQ, **f32) for _ in range(3)]            # KL, LSE1, LSE2 from the first build
+    if loaded[0].streamkl_fwd(*base, *(t.data_ptr() for t in state), s) != 0:
+        raise RuntimeError("forward failed")
+    kl, l1, l2 = (t.data_ptr() for t in state)
+    need = loaded[0].streamkl_workspace_bytes(0, NQ, NK, H, d, 0, 0)
+    ws = torch.empty(max(16, need), device="cuda", dtype=torch.uint8)
+
+    def outputs(call):
+        if call in ("fwd", "splitk"):
+            return [torch.empty(H, NQ, **f32) for _ in range(3)]
+        n = NK if call.startswith("dk") else NQ
+        return [torch.empty(H, n, d, **f32) for _ in range(2 if call.endswith("both") else 1)]
+
+    def launcher(lib, call, out):
+        p = [t.data_ptr() for t in out]
+        if call == "fwd":
+            return lambda: lib.streamkl_fwd(*base, *p, s)
+        if call == "splitk":
+            return lambda: lib.streamkl_fwd_splitk(*base, 0, *p, ws.data_ptr(), ws.numel(), s)
+        path = _lib.BWD_DK_ONLY if call.startswith("dk") else _lib.BWD_DQ_ONLY
+        if call == "dk_both":
+            return lambda: lib.streamkl_bwd_both(*base, l1, l2, kl, None, None, p[0], None, p[1], path, s)
+        if call == "dq_both":
+            return lambda: lib.streamkl_bwd_both(*base, l1, l2, kl, None, p[0], None, p[1], None, path, s)
+        g = p[0]
+        if call in ("dk1", "dq1"):                        # Setting 1: gradients of Q2, K2
+            dq, dk = (g, None) if call == "dq1" else (None, g)
+            return lambda: lib.streamkl_bwd_set1(*base, l1, l2, None, dq, dk, path, None, 0, s)
+        if call in ("dk2", "dq2"):                        # Setting 2: gradients of Q1, K1
+            dq, dk = (g, None) if call == "dq2" else (None, g)
+            return lambda: lib.streamkl_bwd_set2(*base, l1, l2, kl, None, dq, dk, path, None, 0, s)
+        raise ValueError(f"unknown call {call!r} (fwd, splitk, dk_both, dq_both, dk1, dq1, dk2, dq2)")
+
+    for call in calls:
+        outs = [outputs(call) for _ in loaded]
+        runs = [launcher(lib, call, o) for lib, o in zip(loaded, outs)]
+        for r in runs:
+            if r() != 0:
+                raise RuntimeError(f"{call} failed")
+        torch.cuda.synchronize()
+        equal = all(torch.equal(a, b) for o in outs[1:] for a, b in zip(outs[0], o))
+        rel = max(float((a - b).abs().max() / a.abs().max().clamp_min(1e-30)) for o in outs[1:]
+                  for a, b in zip(outs[0], o)) if len(outs) > 1 else 0.0
+        times = [[] for _ in loaded]
+        for rnd in range(rounds):
+            order = list(range(len(loaded)))
+            for i in (order if rnd % 2 == 0 else order[::-1]):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                runs[i]()
+                e0.record(stream)
+                for _ in range(per):
+                    runs[i]()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times[i].append(e0.elapsed_time(e1) / per)
+        med = [float(np.median(t)) for t in times]
+        print(json.dumps({"ab": call, "workload": workload, "libs": libs, "median_ms": [round(m, 4) for m in med],
+                          "ratio_vs_first": [round(m / med[0], 4) for m in med], "bitwise_equal": equal,
+                          "max_rel_diff": rel, "rounds": rounds, "launches_per_round": per}), flush=True)
+        del outs, runs
+    del q1, k1, q2, k2, ws, state
+    torch.cuda.empty_cache()
+
+
 def calibrate_mode(reps: int = 5, mfma_seconds: float = 3.0):
     """The calibration probes (libstreamkl_probes.so): bf16 MFMA loops at 1 to
     3 waves per SIMD (sustained, with board watts), a v_exp_f32 stream, a plain
@@ -822,6 +925,11 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
                     help="run the calibration probes (MFMA loop, v_exp_f32, HBM read, fp32 atomics)")
+    ap.add_argument("--ab", metavar="LIB_A,LIB_B",
+                    help="time two builds of libstreamkl.so against each other in one process (with --workload, "
+                         "--ab-calls); see ab_mode")
+    ap.add_argument("--ab-calls", help="comma-separated: fwd, splitk, dk_both, dq_both, dk1, dq1, dk2, dq2")
+    ap.add_argument("--ab-rounds", type=int, default=8)
     ap.add_argument("--power", action="store_true",
                     help="board power while each kernel of the 64K causal step runs back to back, and probes")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -851,6 +959,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if args.ab:
+        ab_mode(args.ab.split(","), args.workload or "causal64k",
+                args.ab_calls.split(",") if args.ab_calls else None, args.ab_rounds)
+        return
     if args.calibrate:
         calibrate_mode()
         return
