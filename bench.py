@@ -712,18 +712,20 @@ def calibrate_mode(reps: int = 5, mfma_seconds: float = 3.0):
     # long enough for the board to settle at its power limit), at 1, 2 and 3
     # waves per SIMD: one workgroup per CU per wave-per-SIMD, all resident at
     # once, ~10 ms per call.  Constant operands, then realistic ones (random
-    # bf16 changing on every MFMA) from registers and with A from LDS.
+    # bf16 changing on every MFMA) from registers, with A from LDS (one b128 read
+    # per lane per MFMA) and with A from LDS through transposing reads.
     wg_max = 4 * cus
     sink = torch.empty(wg_max * T, device="cuda")
     src = torch.randn(wg_max * T * 128, device="cuda").to(torch.bfloat16)   # 256 bytes per thread
     best = 0.0
-    for kind, per_trip, base_iters in (("const", 4, 150000), ("random_regs", 8, 75000), ("random_lds", 8, 75000)):
+    for kind, per_trip, base_iters in (("const", 4, 150000), ("random_regs", 8, 75000), ("random_lds", 8, 75000),
+                                       ("random_ldstr", 8, 75000)):
         for wps in (1, 2, 3):
             wg, iters = wps * cus, base_iters // wps
             if kind == "const":
                 launch = lambda: P.streamkl_probe_mfma(wps, wg, iters, sink.data_ptr(), sink.numel(), s)
             else:
-                lds = int(kind == "random_lds")
+                lds = {"random_regs": 0, "random_lds": 1, "random_ldstr": 2}[kind]
                 launch = lambda: P.streamkl_probe_mfma_data(src.data_ptr(), src.numel() * 2, lds, wps, wg, iters,
                                                             sink.data_ptr(), sink.numel(), s)
             if launch() != 0:

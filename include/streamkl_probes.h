@@ -44,8 +44,10 @@ int streamkl_probe_mfma(int waves_per_simd, int workgroups, int iters, float* si
 
 /* As streamkl_probe_mfma, but each lane cycles through 8 A and 8 B operand
  * chunks read from src (src_bytes >= workgroups * threads * 256, 16-byte
- * aligned); from_lds != 0 takes the A operand from a 32 KB LDS tile of that
- * data instead.  8 MFMAs of 32768 flop per wave per loop trip. */
+ * aligned); from_lds = 1 takes the A operand from a 32 KB LDS tile of that
+ * data instead (one ds_read_b128 per lane per MFMA), from_lds = 2 the same
+ * bytes through two transposing reads (ds_read_b64_tr_b16).  8 MFMAs of
+ * 32768 flop per wave per loop trip. */
 int streamkl_probe_mfma_data(const void* src, size_t src_bytes, int from_lds, int waves_per_simd, int workgroups,
                              int iters, float* sink, size_t sink_floats, hipStream_t stream);
 

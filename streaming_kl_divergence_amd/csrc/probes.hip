@@ -64,14 +64,28 @@ __global__ __launch_bounds__(kThreads) void mfma_loop(int iters, float* __restri
   store_through_lds<WPS>(lds, s, sink, gid);
 }
 
+// 16 bytes at tile[idx] (idx < 2048) through two transposing 8-byte reads.
+__device__ __forceinline__ u32x4 read_tr_16(const u32x4* tile, int idx) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const __attribute__((address_space(3))) char* p = (const __attribute__((address_space(3))) char*)(tile + idx);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p + 8));
+  const u32x2 l = __builtin_bit_cast(u32x2, lo), h = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l.x, l.y, h.x, h.y};
+}
+
 // The same MFMA loop with realistic operands: each lane holds 8 different A
 // and B chunks loaded from `src` (caller-supplied data, 256 bytes per thread),
 // so the multiplier inputs change on every instruction as they do on real
-// tiles.  LDS = true: the A operand comes from a 32 KB LDS tile of the same
-// data instead (16 bytes per lane per MFMA, the score-MFMA access pattern).
-template <bool LDS, int WPS>
+// tiles.  SRC 1: the A operand comes from a 32 KB LDS tile of the same data
+// instead (one 16-byte ds_read_b128 per lane per MFMA, the score-MFMA access
+// pattern); SRC 2: the same bytes through two transposing 8-byte reads
+// (ds_read_b64_tr_b16, the gradient-MFMA access pattern of the backward).
+template <int SRC, int WPS>
 __global__ __launch_bounds__(kThreads) void mfma_data_loop(const u32x4* __restrict__ src, int iters,
                                                           float* __restrict__ sink) {
+  constexpr bool LDS = SRC != 0;
   static_assert(reserve_bytes<WPS>() >= 2048 * 16, "the LDS tile lives in the reservation");
   __shared__ u32x4 tile[reserve_bytes<WPS>() / 16];
   const int gid = blockIdx.x * kThreads + threadIdx.x;
@@ -92,12 +106,18 @@ __global__ __launch_bounds__(kThreads) void mfma_data_loop(const u32x4* __restri
 #pragma unroll
     for (int i = 0; i < 8; i += 4) {
       u32x4 x0 = a[i], x1 = a[i + 1], x2 = a[i + 2], x3 = a[i + 3];
-      if (LDS) {
+      if (SRC == 1) {
         const int o = (it * 8 + i) * 64 + lane;
         x0 = tile[o & 2047];
         x1 = tile[(o + 64) & 2047];
         x2 = tile[(o + 128) & 2047];
         x3 = tile[(o + 192) & 2047];
+      } else if (SRC == 2) {
+        const int o = (it * 8 + i) * 64 + lane;
+        x0 = read_tr_16(tile, o & 2047);
+        x1 = read_tr_16(tile, (o + 64) & 2047);
+        x2 = read_tr_16(tile, (o + 128) & 2047);
+        x3 = read_tr_16(tile, (o + 192) & 2047);
       }
       c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x0), __builtin_bit_cast(bf16x8, b[i]),
                                                     c0, 0, 0, 0);
@@ -213,15 +233,15 @@ __global__ __launch_bounds__(kThreads) void atomic_loop(float* __restrict__ dst,
 
 int status(hipError_t e) { return e == hipSuccess ? 0 : -6; }
 
-template <bool LDS>
+template <int SRC>
 hipError_t launch_mfma_data(int waves_per_simd, int workgroups, const u32x4* src, int iters, float* sink,
                             hipStream_t stream) {
   if (waves_per_simd == 1)
-    hipLaunchKernelGGL((mfma_data_loop<LDS, 1>), dim3(workgroups), dim3(kThreads), 0, stream, src, iters, sink);
+    hipLaunchKernelGGL((mfma_data_loop<SRC, 1>), dim3(workgroups), dim3(kThreads), 0, stream, src, iters, sink);
   else if (waves_per_simd == 2)
-    hipLaunchKernelGGL((mfma_data_loop<LDS, 2>), dim3(workgroups), dim3(kThreads), 0, stream, src, iters, sink);
+    hipLaunchKernelGGL((mfma_data_loop<SRC, 2>), dim3(workgroups), dim3(kThreads), 0, stream, src, iters, sink);
   else
-    hipLaunchKernelGGL((mfma_data_loop<LDS, 3>), dim3(workgroups), dim3(kThreads), 0, stream, src, iters, sink);
+    hipLaunchKernelGGL((mfma_data_loop<SRC, 3>), dim3(workgroups), dim3(kThreads), 0, stream, src, iters, sink);
   return hipGetLastError();
 }
 
@@ -247,13 +267,15 @@ int streamkl_probe_mfma(int waves_per_simd, int workgroups, int iters, float* si
 
 int streamkl_probe_mfma_data(const void* src, size_t src_bytes, int from_lds, int waves_per_simd, int workgroups,
                              int iters, float* sink, size_t sink_floats, hipStream_t stream) {
-  if (!src || waves_per_simd < 1 || waves_per_simd > 3 || workgroups < 1 || iters < 1 || !sink ||
+  if (!src || from_lds < 0 || from_lds > 2 || waves_per_simd < 1 || waves_per_simd > 3 || workgroups < 1 ||
+      iters < 1 || !sink ||
       sink_floats < (size_t)workgroups * kThreads || ((uintptr_t)src & 15) != 0 ||
       src_bytes < (size_t)workgroups * kThreads * 256)
     return -1;
   const u32x4* s = (const u32x4*)src;
-  return status(from_lds ? launch_mfma_data<true>(waves_per_simd, workgroups, s, iters, sink, stream)
-                         : launch_mfma_data<false>(waves_per_simd, workgroups, s, iters, sink, stream));
+  if (from_lds == 2) return status(launch_mfma_data<2>(waves_per_simd, workgroups, s, iters, sink, stream));
+  if (from_lds == 1) return status(launch_mfma_data<1>(waves_per_simd, workgroups, s, iters, sink, stream));
+  return status(launch_mfma_data<0>(waves_per_simd, workgroups, s, iters, sink, stream));
 }
 
 int streamkl_probe_exp(int workgroups, int iters, float* sink, size_t sink_floats, hipStream_t stream) {
