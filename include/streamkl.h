@@ -160,9 +160,6 @@ int streamkl_fwd_splitk_noalloc(const void* q1, const void* k1, const void* q2, 
  * head_dim]), overwriting them.  lse1, lse2 are the forward's outputs for the
  * same inputs.  `path` picks the fused or separate kernels (AUTO: the
  * library's choice); DK_ONLY / DQ_ONLY compute one of the two gradients.
- * FUSED with fp32 inputs and head_dim 128 is STREAMKL_ERR_UNSUPPORTED (its
- * tiles of dS and K^T do not fit one workgroup's 160 KB of LDS); AUTO never
- * picks it.
  * Calling DK_ONLY then DQ_ONLY gives the same result as SEPARATE.
  * workspace: at least streamkl_workspace_bytes(1, ...) bytes (may be NULL
  * when that is 0, which it is for every shape today).

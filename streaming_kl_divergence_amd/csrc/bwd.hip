@@ -197,7 +197,7 @@ void bwd_kv_kernel(BwdParams p) {
   SKL_LDS char* qt = lds + 4 * TILE;                                    // fp32 only
   SKL_LDS float* coef = (SKL_LDS float*)(qt + C::kQtBytes);             // [2][3][BT]
   SKL_LDS char* kt = (SKL_LDS char*)(coef + 2 * 3 * BT);
-  SKL_LDS char* dst = kt + C::KT::kBytes;
+  SKL_LDS char* dst = kt + C::KT::kBytes;   // dS block (fused), unless it reuses the Q tiles
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -296,6 +296,7 @@ void bwd_kv_kernel(BwdParams p) {
     const SKL_LDS char* t1 = lds + buf * 2 * TILE;
     const SKL_LDS char* t2 = t1 + TILE;
     const SKL_LDS float* cf = coef + buf * 3 * BT;
+    SKL_LDS char* dsb = C::kDsInTiles ? lds + buf * 2 * TILE : dst;
     wait_async_loads();
     __syncthreads();  // tile t and its coefficients visible; tile t-1's readers done
     const bool has_next = t + 1 < ntiles;
@@ -325,6 +326,14 @@ void bwd_kv_kernel(BwdParams p) {
     }
     const int qlast = min(q0 + BT, p.n_q) - 1;
     const bool skip = wave_idle || (p.causal && kw0 > qlast + off);
+    // dS kept in registers until every wave is done with the Q tiles it will overwrite
+    float dsk[C::kDsInTiles ? NQB : 1][16];
+    if constexpr (FUSED && C::kDsInTiles) {
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dsk[qb][r] = 0.f;
+    }
     if (!skip) {
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
@@ -372,7 +381,10 @@ void bwd_kv_kernel(BwdParams p) {
           else
             dkt[db] = kgroup_mfma<T>(qt + (db * 32 + col) * C::QT::kStride, qb * 32, h, ds, dkt[db]);
         }
-        if (FUSED) {
+        if constexpr (FUSED && C::kDsInTiles) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dsk[qb][r] = ds[r];
+        } else if (FUSED) {
           // this dS block -> LDS as [query][key]
           const int kl = wave * 32 + col;
 #pragma unroll
@@ -382,7 +394,7 @@ void bwd_kv_kernel(BwdParams p) {
           }
         }
       }
-    } else if (FUSED) {
+    } else if (FUSED && !C::kDsInTiles) {
       // nothing to add from these keys: their dS columns are zero
       const int kl = wave * 32 + col;
 #pragma unroll
@@ -391,6 +403,17 @@ void bwd_kv_kernel(BwdParams p) {
         for (int r = 0; r < 16; ++r) {
           const int ql = qb * 32 + acc_row(r, h);
           *(SKL_LDS T*)(dst + ql * C::DS::kStride + kl * (int)sizeof(T)) = (T)0.f;
+        }
+    }
+    if constexpr (FUSED && C::kDsInTiles) {
+      __syncthreads();   // every wave's scores are done: the Q tiles may be overwritten
+      const int kl = wave * 32 + col;
+#pragma unroll
+      for (int qb = 0; qb < NQB; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ql = qb * 32 + acc_row(r, h);
+          *(SKL_LDS T*)(dsb + ql * C::DS::kStride + kl * (int)sizeof(T)) = (T)dsk[qb][r];
         }
     }
     if (FUSED) {
@@ -402,7 +425,7 @@ void bwd_kv_kernel(BwdParams p) {
       for (int b = wave; b < NB; b += NW) {
         const int qblk = b / DB, db = b % DB;
         f32x16 acc = f32x16{};
-        const SKL_LDS char* arow = dst + (qblk * 32 + col) * C::DS::kStride + h * 16;
+        const SKL_LDS char* arow = dsb + (qblk * 32 + col) * C::DS::kStride + h * 16;
         const SKL_LDS char* brow = kt + (db * 32 + col) * C::KT::kStride + h * 16;
 #pragma unroll
         for (int g = 0; g < DSG; ++g)

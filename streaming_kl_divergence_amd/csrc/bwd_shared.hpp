@@ -31,7 +31,14 @@ struct KvCfg {
   using DS = TGeom<T, BT, BKW, 16>;   // dS rows: [query][key]
   static constexpr int kQtBytes = TR ? 0 : QT::kBytes;
   static constexpr int kLdsBase = 4 * TILE + kQtBytes + 2 * 3 * BT * 4;
-  static constexpr int kLdsFused = kLdsBase + KT::kBytes + DS::kBytes;
+  // The fused kernel's dS block has a region of its own when it fits beside
+  // the rest in a CU's 160 KB; otherwise (fp32 at d = 128) it reuses the two
+  // Q tiles of the current buffer, dead once every wave has its scores (the
+  // kernel adds one barrier before writing dS there).
+  static constexpr bool kDsInTiles = kLdsBase + KT::kBytes + DS::kBytes > 160 * 1024;
+  static_assert(!kDsInTiles || (DS::kBytes <= 2 * TILE && NQB == 1),
+                "dS reuses one buffer's two Q tiles only with one query block per tile");
+  static constexpr int kLdsFused = kLdsBase + KT::kBytes + (kDsInTiles ? 0 : DS::kBytes);
 };
 
 template <typename T, int D>

@@ -146,17 +146,6 @@ def test_backward_validation():
     assert lib.streamkl_bwd_set2(*bad, FAKE, None, FAKE, FAKE, 0, None, 0, None) == L.ERR_SHAPE
 
 
-def test_fused_fp32_d128_is_unsupported():
-    """The fused kernel's LDS footprint does not fit fp32 with head_dim 128:
-    the call is refused before any launch, for both settings; AUTO stays on
-    the separate kernels there."""
-    lib = L.lib()
-    base = [FAKE] * 4 + [16, 16, 2, 128, 0, 0.125, L.FP32, FAKE, FAKE]
-    assert lib.streamkl_bwd_set1(*base, None, FAKE, FAKE, L.BWD_FUSED, None, 0, None) == L.ERR_UNSUPPORTED
-    assert lib.streamkl_bwd_set2(*base, FAKE, None, FAKE, FAKE, L.BWD_FUSED, None, 0, None) == L.ERR_UNSUPPORTED
-    assert lib.streamkl_bwd_select(16, 16, 2, 128, 0) == L.BWD_SEPARATE
-
-
 def test_both_settings_validation():
     lib = L.lib()
     base = [FAKE] * 4 + [16, 16, 2, 64, 1, 0.125, L.BF16, FAKE, FAKE]

@@ -22,11 +22,11 @@ out = {
     "ws0": lib.streamkl_workspace_bytes(0, 1, 4096, 2, 128, 0, 0),
     "ws3": lib.streamkl_workspace_bytes(0, 1, 4096, 2, 128, 3, 0),
     "select": lib.streamkl_bwd_select(4096, 4096, 2, 128, 1),
-    # rejected before launch: NULL output, workspace too small, fused fp32 d=128
+    # rejected before launch: NULL output, workspace too small, unknown backward path
     "fwd_null": lib.streamkl_fwd(F, F, F, F, 16, 16, 2, 64, 0, 0.125, L.BF16, None, F, F, None),
     "splitk_ws": lib.streamkl_fwd_splitk(F, F, F, F, 1, 4096, 2, 128, 0, 0.125, L.BF16, 0, F, F, F, F, 16, None),
-    "bwd_fused": lib.streamkl_bwd_set1(F, F, F, F, 16, 16, 2, 128, 0, 0.125, L.FP32, F, F, None, F, F,
-                                       L.BWD_FUSED, None, 0, None),
+    "bwd_path": lib.streamkl_bwd_set1(F, F, F, F, 16, 16, 2, 128, 0, 0.125, L.FP32, F, F, None, F, F,
+                                      9, None, 0, None),
 }
 sys.stderr.flush()
 print(json.dumps(out))
@@ -51,7 +51,7 @@ def test_defaults_print_nothing():
     assert out["select"] == 2                       # separate
     assert out["ws0"] == out["auto"] * 2 * 1 * 20   # splits x heads x n_q x 5 floats
     assert out["ws3"] == 3 * 2 * 1 * 20
-    assert (out["fwd_null"], out["splitk_ws"], out["bwd_fused"]) == (-1, -5, -3)
+    assert (out["fwd_null"], out["splitk_ws"], out["bwd_path"]) == (-1, -5, -3)
     assert log_lines(err) == []
 
 
