@@ -22,9 +22,12 @@ operands under the board power limit, the HBM read rate, fp32 atomics) come from
 (hipBLASLt) as platform context (parts.gemm_bf16_16384_tflops).
 
 Usage:
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--gemm-ref] [--no-decode]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--gemm-ref] [--no-decode] [--no-ceiling]
       the one-line benchmark of the 64K causal step (the default); parts.decode512k
-      carries the 512K-key split-K decode's HBM read rate, timed in the same run.
+      carries the 512K-key split-K decode's HBM read rate, timed in the same run;
+      parts.mfma_ceiling the matrix cores' sustained rate on this GPU with the
+      step kernels' operand pattern, and each kernel's executed rate as a
+      fraction of it (a figure that does not depend on which board ran).
   python bench.py --configs
       one JSON line per workload (tiny fp32, 8K causal, 64K causal with both
       backward paths and the both-settings backward, 512K decode split-K vs
@@ -811,6 +814,37 @@ def cpu_baseline():
                       f"Setting 2, fp64 numpy/BLAS; {dt:.1f} s for {flop / 1e12:.3f} TFLOP"}
 
 
+def ceiling_part(seconds: float = 4.0) -> dict:
+    """The matrix cores' sustained rate on this GPU with the operand pattern of
+    the step's kernels (random bf16 operands, one of them streamed from LDS for
+    every MFMA), measured beside the step: one wave per SIMD, as in the
+    both-settings kernels, and two, as in the forward and the single-setting
+    kernels.  Each probe runs back to back for `seconds` so the board settles
+    at its power limit.  Boards of the pool differ by up to ~12% in the work
+    that power buys; a kernel's rate divided by the probe's on the same board
+    does not."""
+    import torch
+    from streaming_kl_divergence_amd import _lib
+    P = _lib.probes()
+    T = P.streamkl_probe_threads()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    s = torch.cuda.current_stream().cuda_stream
+    src = torch.randn(2 * cus * T * 128, device="cuda").to(torch.bfloat16)   # 256 bytes per thread
+    sink = torch.empty(2 * cus * T, device="cuda")
+    out = {}
+    for wps in (1, 2):
+        wg, iters = wps * cus, 75000 // wps
+        launch = lambda: P.streamkl_probe_mfma_data(src.data_ptr(), src.numel() * 2, 1, wps, wg, iters,
+                                                    sink.data_ptr(), sink.numel(), s)
+        if launch() != 0:
+            raise RuntimeError("probe launch failed")
+        ms, _, _ = _loop_for(launch, seconds)
+        out[f"lds_operand_{wps}_wave_per_simd_tflops"] = round(wg * 4 * iters * 8 * 32768 / (ms * 1e-3) / 1e12, 1)
+    del src, sink
+    torch.cuda.empty_cache()
+    return out
+
+
 def decode_part(reps: int = 20) -> dict:
     """The 512K-key decode workload (32 heads, one query, split-K with the
     automatic count) timed beside the step: HBM read rate of its inputs."""
@@ -918,6 +952,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gemm-ref", action="store_true", help="also time a 16384^3 bf16 GEMM (torch.mm) as context")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the matrix-core probe measured beside the step (parts.mfma_ceiling)")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the 512K-key split-K decode measured beside the step (parts.decode512k)")
     ap.add_argument("--no-gemm-ref", action="store_true", help=argparse.SUPPRESS)   # the default; kept for old commands
@@ -1089,6 +1125,16 @@ def main():
                 "traffic": measured_traffic(kname),
                 "avg_launch_ms": round(float(mean_call[j]), 3),
                 "work_per_launch": f"{kflop}*d flop x {E} unmasked pairs = {kflop * d * E / 1e12:.3f} TFLOP"}
+    if not args.no_ceiling:
+        # each kernel's executed MFMA rate (k*d flop per pair, as it runs)
+        # against the probe at its occupancy: the both-settings and fused
+        # kernels run one wave per SIMD, the others two
+        ceil = ceiling_part()
+        for name, k in calls:
+            wps = 1 if ("both" in name or "fused" in name) else 2
+            ceil[f"{name}_frac"] = round(k * d * E / (parts[name]["ms"] * 1e-3) / 1e12
+                                         / ceil[f"lds_operand_{wps}_wave_per_simd_tflops"], 3)
+        parts["mfma_ceiling"] = ceil
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
