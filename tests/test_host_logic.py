@@ -130,3 +130,35 @@ def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 1 and "one GPU" in r.stderr
+
+
+def _undefined_names(path):
+    """Names a function reads that nothing defines: not a local, a module-level
+    name or a builtin (symtable's view; catches what only a GPU run would
+    otherwise reach, such as a variable left over from an edit)."""
+    import builtins
+    import symtable
+    with open(path) as f:
+        top = symtable.symtable(f.read(), path, "exec")
+    module = {s.get_name() for s in top.get_symbols() if s.is_assigned() or s.is_imported() or s.is_namespace()}
+    bad = []
+
+    def walk(t):
+        for s in t.get_symbols():
+            n = s.get_name()
+            if (s.is_referenced() and s.is_global() and not s.is_declared_global() and n not in module
+                    and not hasattr(builtins, n) and n not in ("__file__", "__name__")):
+                bad.append((t.get_name(), t.get_lineno(), n))
+        for c in t.get_children():
+            walk(c)
+    walk(top)
+    return bad
+
+
+def test_python_sources_reference_no_undefined_names():
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    files = ["bench.py", "__graft_entry__.py", "workloads/__init__.py"]
+    for d in ("streaming_kl_divergence_amd", "oracle", "tests"):
+        files += [os.path.join(d, f) for f in sorted(os.listdir(os.path.join(root, d))) if f.endswith(".py")]
+    found = {f: _undefined_names(os.path.join(root, f)) for f in files}
+    assert not any(found.values()), {f: b for f, b in found.items() if b}
