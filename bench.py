@@ -109,18 +109,26 @@ def upload(w: W.Workload, threads: int):
     return out
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace collapsed."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
     """Hash of the attention-KL library's device code (its .hip sources and
-    the headers beside them).  Host-only files such as the C ABI's argument
-    checks, and the calibration probes (a library of their own), do not change
-    what a kernel moves."""
+    the headers beside them, comments and layout ignored).  Host-only files
+    such as the C ABI's argument checks, and the calibration probes (a library
+    of their own), do not change what a kernel moves."""
     from streaming_kl_divergence_amd.build import SOURCES
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "streaming_kl_divergence_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if (f.endswith(".hip") and f in SOURCES) or f.endswith(".hpp"):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(fh.read())
+            with open(os.path.join(csrc, f)) as fh:
+                h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

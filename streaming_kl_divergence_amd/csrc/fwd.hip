@@ -29,7 +29,11 @@
 //     the key range take the masked code path.
 //   * Each XCD walks a contiguous run of (head, query block) items, one head
 //     at a time (xcd_work_index), so the workgroups resident on an XCD stream
-//     the same K tiles through its L2.
+//     the same K tiles through its L2; split-K walks (head, key range, query
+//     block) items, so the workgroups of one key range run side by side.
+//   * When a head has a single query block (decode and other short query
+//     sets) every key is read by one workgroup only, and the tiles are loaded
+//     with the non-temporal cache policy.
 #include <limits.h>
 
 #include <mutex>
