@@ -1158,11 +1158,15 @@ def main():
         # each kernel's executed MFMA rate (k*d flop per pair, as it runs)
         # against the probe at its occupancy: the both-settings and fused
         # kernels run one wave per SIMD, the others two
-        ceil = ceiling_part()
-        for name, k in calls:
-            wps = 1 if ("both" in name or "fused" in name) else 2
-            ceil[f"{name}_frac"] = round(k * d * E / (parts[name]["ms"] * 1e-3) / 1e12
-                                         / ceil[f"lds_operand_{wps}_wave_per_simd_tflops"], 3)
+        try:
+            ceil = ceiling_part()
+        except ImportError as e:   # the probes are a library of their own; the step does not need them
+            ceil = {"skipped": str(e)}
+        else:
+            for name, k in calls:
+                wps = 1 if ("both" in name or "fused" in name) else 2
+                ceil[f"{name}_frac"] = round(k * d * E / (parts[name]["ms"] * 1e-3) / 1e12
+                                             / ceil[f"lds_operand_{wps}_wave_per_simd_tflops"], 3)
         parts["mfma_ceiling"] = ceil
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
