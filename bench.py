@@ -750,20 +750,27 @@ def calibrate_mode(reps: int = 5, mfma_seconds: float = 3.0):
     sink = torch.empty(wg_max * T, device="cuda")
     src = torch.randn(wg_max * T * 128, device="cuda").to(torch.bfloat16)   # 256 bytes per thread
     best = 0.0
+    # The reuse kinds repeat the register B chunk across consecutive MFMAs
+    # (pairs, with A from registers or LDS; fours, registers): whether an
+    # operand that stays put between instructions saves energy.
+    modes = {"random_regs": 0, "random_lds": 1, "random_ldstr": 2, "random_lds_bpairs": 3, "random_regs_bpairs": 4,
+             "random_regs_bquads": 5}
     for kind, per_trip, base_iters in (("const", 4, 150000), ("random_regs", 8, 75000), ("random_lds", 8, 75000),
-                                       ("random_ldstr", 8, 75000)):
+                                       ("random_ldstr", 8, 75000), ("random_regs_bpairs", 8, 75000),
+                                       ("random_regs_bquads", 8, 75000), ("random_lds_bpairs", 8, 75000)):
         for wps in (1, 2, 3):
             wg, iters = wps * cus, base_iters // wps
             if kind == "const":
                 launch = lambda: P.streamkl_probe_mfma(wps, wg, iters, sink.data_ptr(), sink.numel(), s)
             else:
-                lds = {"random_regs": 0, "random_lds": 1, "random_ldstr": 2}[kind]
+                lds = modes[kind]
                 launch = lambda: P.streamkl_probe_mfma_data(src.data_ptr(), src.numel() * 2, lds, wps, wg, iters,
                                                             sink.data_ptr(), sink.numel(), s)
             if launch() != 0:
                 raise RuntimeError("probe launch failed")
             ms, a, b = _loop_for(launch, mfma_seconds)
             tf = wg * 4 * iters * per_trip * 32768 / (ms * 1e-3) / 1e12
+            print(f"calibrate: mfma {kind} at {wps} wave(s)/SIMD {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
             out[f"mfma_bf16_{kind}_w{wps}_tflops"] = round(tf, 1)
             out[f"mfma_bf16_{kind}_w{wps}_watts"] = ps.median(a, b)
             if kind != "const":

@@ -46,8 +46,11 @@ int streamkl_probe_mfma(int waves_per_simd, int workgroups, int iters, float* si
  * chunks read from src (src_bytes >= workgroups * threads * 256, 16-byte
  * aligned); from_lds = 1 takes the A operand from a 32 KB LDS tile of that
  * data instead (one ds_read_b128 per lane per MFMA), from_lds = 2 the same
- * bytes through two transposing reads (ds_read_b64_tr_b16).  8 MFMAs of
- * 32768 flop per wave per loop trip. */
+ * bytes through two transposing reads (ds_read_b64_tr_b16).  Operand reuse:
+ * from_lds = 3 is mode 1 with each B chunk used by two consecutive MFMAs,
+ * 4 the same pairing with both operands in registers, 5 one B chunk for four
+ * consecutive MFMAs (registers).  Any other value is rejected (-1).  8 MFMAs
+ * of 32768 flop per wave per loop trip in every mode. */
 int streamkl_probe_mfma_data(const void* src, size_t src_bytes, int from_lds, int waves_per_simd, int workgroups,
                              int iters, float* sink, size_t sink_floats, hipStream_t stream);
 

@@ -82,10 +82,14 @@ __device__ __forceinline__ u32x4 read_tr_16(const u32x4* tile, int idx) {
 // instead (one 16-byte ds_read_b128 per lane per MFMA, the score-MFMA access
 // pattern); SRC 2: the same bytes through two transposing 8-byte reads
 // (ds_read_b64_tr_b16, the gradient-MFMA access pattern of the backward).
+// Operand reuse: SRC 3 is SRC 1 with each B chunk used by two consecutive
+// MFMAs (two key blocks against one register-held query chunk); SRC 4 the
+// same pairing from registers only; SRC 5 one B chunk for four consecutive
+// MFMAs, from registers.  The MFMA count is the same in every mode.
 template <int SRC, int WPS>
 __global__ __launch_bounds__(kThreads) void mfma_data_loop(const u32x4* __restrict__ src, int iters,
                                                           float* __restrict__ sink) {
-  constexpr bool LDS = SRC != 0;
+  constexpr bool LDS = SRC == 1 || SRC == 2 || SRC == 3;
   static_assert(reserve_bytes<WPS>() >= 2048 * 16, "the LDS tile lives in the reservation");
   __shared__ u32x4 tile[reserve_bytes<WPS>() / 16];
   const int gid = blockIdx.x * kThreads + threadIdx.x;
@@ -106,7 +110,7 @@ __global__ __launch_bounds__(kThreads) void mfma_data_loop(const u32x4* __restri
 #pragma unroll
     for (int i = 0; i < 8; i += 4) {
       u32x4 x0 = a[i], x1 = a[i + 1], x2 = a[i + 2], x3 = a[i + 3];
-      if (SRC == 1) {
+      if (SRC == 1 || SRC == 3) {
         const int o = (it * 8 + i) * 64 + lane;
         x0 = tile[o & 2047];
         x1 = tile[(o + 64) & 2047];
@@ -119,14 +123,17 @@ __global__ __launch_bounds__(kThreads) void mfma_data_loop(const u32x4* __restri
         x2 = read_tr_16(tile, (o + 128) & 2047);
         x3 = read_tr_16(tile, (o + 192) & 2047);
       }
-      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x0), __builtin_bit_cast(bf16x8, b[i]),
+      constexpr bool PAIR = SRC == 3 || SRC == 4, QUAD = SRC == 5;
+      const u32x4 y0 = b[i], y1 = (PAIR || QUAD) ? b[i] : b[i + 1];
+      const u32x4 y2 = QUAD ? b[i] : b[i + 2], y3 = QUAD ? b[i] : PAIR ? b[i + 2] : b[i + 3];
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x0), __builtin_bit_cast(bf16x8, y0),
                                                     c0, 0, 0, 0);
-      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x1),
-                                                    __builtin_bit_cast(bf16x8, b[i + 1]), c1, 0, 0, 0);
-      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x2),
-                                                    __builtin_bit_cast(bf16x8, b[i + 2]), c2, 0, 0, 0);
-      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x3),
-                                                    __builtin_bit_cast(bf16x8, b[i + 3]), c3, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x1), __builtin_bit_cast(bf16x8, y1),
+                                                    c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x2), __builtin_bit_cast(bf16x8, y2),
+                                                    c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x3), __builtin_bit_cast(bf16x8, y3),
+                                                    c3, 0, 0, 0);
       // Register operands: keep the loop's scalar bookkeeping out from between
       // the MFMAs.  With two or three waves per SIMD, a scalar instruction
       // between them measurably lowers the rate this loop sustains, below the
@@ -267,12 +274,15 @@ int streamkl_probe_mfma(int waves_per_simd, int workgroups, int iters, float* si
 
 int streamkl_probe_mfma_data(const void* src, size_t src_bytes, int from_lds, int waves_per_simd, int workgroups,
                              int iters, float* sink, size_t sink_floats, hipStream_t stream) {
-  if (!src || from_lds < 0 || from_lds > 2 || waves_per_simd < 1 || waves_per_simd > 3 || workgroups < 1 ||
+  if (!src || from_lds < 0 || from_lds > 5 || waves_per_simd < 1 || waves_per_simd > 3 || workgroups < 1 ||
       iters < 1 || !sink ||
       sink_floats < (size_t)workgroups * kThreads || ((uintptr_t)src & 15) != 0 ||
       src_bytes < (size_t)workgroups * kThreads * 256)
     return -1;
   const u32x4* s = (const u32x4*)src;
+  if (from_lds == 5) return status(launch_mfma_data<5>(waves_per_simd, workgroups, s, iters, sink, stream));
+  if (from_lds == 4) return status(launch_mfma_data<4>(waves_per_simd, workgroups, s, iters, sink, stream));
+  if (from_lds == 3) return status(launch_mfma_data<3>(waves_per_simd, workgroups, s, iters, sink, stream));
   if (from_lds == 2) return status(launch_mfma_data<2>(waves_per_simd, workgroups, s, iters, sink, stream));
   if (from_lds == 1) return status(launch_mfma_data<1>(waves_per_simd, workgroups, s, iters, sink, stream));
   return status(launch_mfma_data<0>(waves_per_simd, workgroups, s, iters, sink, stream));

@@ -45,7 +45,8 @@ def test_probe_library_exports_and_validates():
     assert lib.streamkl_probe_mfma(4, 4, 10, FAKE, 4 * t, None) == -1              # 1 to 3 waves per SIMD
     assert lib.streamkl_probe_mfma(0, 4, 10, FAKE, 4 * t, None) == -1
     assert lib.streamkl_probe_mfma_data(FAKE, 4 * t * 256, 0, 4, 4, 10, FAKE, 4 * t, None) == -1
-    assert lib.streamkl_probe_mfma_data(FAKE, 4 * t * 256, 3, 1, 4, 10, FAKE, 4 * t, None) == -1   # operand source 0-2
+    assert lib.streamkl_probe_mfma_data(FAKE, 4 * t * 256, 6, 1, 4, 10, FAKE, 4 * t, None) == -1   # operand mode 0-5
+    assert lib.streamkl_probe_mfma_data(FAKE, 4 * t * 256, -1, 1, 4, 10, FAKE, 4 * t, None) == -1
     assert lib.streamkl_probe_mfma_data(FAKE, 4 * t * 256 - 16, 1, 2, 4, 10, FAKE, 4 * t, None) == -1
     assert lib.streamkl_probe_exp(0, 10, FAKE, 4 * t, None) == -1
     assert lib.streamkl_probe_exp_fma(3, 4, 10, FAKE, 4 * 512, None) == -1      # modes 0 to 2
