@@ -184,7 +184,7 @@ __device__ __forceinline__ float dlogit(float x1, float x2, float c, float a, fl
 
 // ---- key-block kernel: dK (separate path) or dK + atomic dQ (fused path) ---------
 
-// bf16 separate path: two waves per SIMD (256 VGPRs); the fp32 and fused
+// bf16 separate path: two waves per SIMD (at most 256 VGPRs each); the fp32 and fused
 // instantiations need more registers and run one wave per SIMD.
 template <typename T, int D, int SETTING, bool FUSED, bool HAS_G>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu((sizeof(T) == 2 && !FUSED) ? 2 : 1)))

@@ -259,7 +259,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdParams p) {
   const int qlim = qrow + off;   // last key this lane's query may see (causal)
   const int pb = pair_base<T, D>(col, h);
 
-  // Two waves per SIMD (223 VGPRs) overlap one wave's MFMAs with the other's VALU.
+  // Two waves per SIMD (212 VGPRs each) overlap one wave's MFMAs with the other's VALU.
   f32x16 s1[NKB], s2[NKB];
   // STREAM: this workgroup holds every query of its head (one query block
   // per head: decode and other short query sets), so no other workgroup reads
