@@ -88,6 +88,12 @@ import numpy as np  # noqa: E402
 import workloads as W  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 (matrix and vector)
+
+
+def peak_tflops(dtype: str) -> float:
+    """Published MI355X peak of the arithmetic a workload's inputs run on."""
+    return PEAK_FP32_TFLOPS if dtype == "fp32" else PEAK_BF16_TFLOPS
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 METRIC = "fwd/bwd TFLOP/s + ms, 32 heads d=128 bf16 causal N=64K; % MFMA peak"
 
@@ -329,11 +335,14 @@ def configs_mode():
             out.update(extra)
         print(json.dumps(out), flush=True)
 
+    cur = {"peak": PEAK_BF16_TFLOPS}   # the peak of the workload being timed
+
     def entry(ms, flop=None, hbm=None):
         e = {"median_ms": round(float(np.median(ms)), 4), "min_ms": round(float(ms.min()), 4), "runs": len(ms)}
         if flop:
+            peak = cur["peak"]
             tf = flop / (np.median(ms) * 1e-3) / 1e12
-            e.update({"tflops": round(float(tf), 1), "pct_peak": round(100 * float(tf) / PEAK_BF16_TFLOPS, 1)})
+            e.update({"tflops": round(float(tf), 1), "pct_peak": round(100 * float(tf) / peak, 1)})
         if hbm:
             gbs = hbm / (np.median(ms) * 1e-3) / 1e9
             e.update({"gbs": round(float(gbs), 1), "pct_hbm": round(100 * float(gbs) / PEAK_HBM_GBS, 1)})
@@ -341,6 +350,7 @@ def configs_mode():
 
     def run(name, settings, paths=("auto",), reps=10, both=False, splitk=False):
         w = W.WORKLOADS[name]
+        cur["peak"] = peak_tflops(w.dtype)
         q1, k1, q2, k2 = upload(w, threads)
         d, E = w.head_dim, w.elements()
         kl, l1, l2 = skl.fwd(q1, k1, q2, k2, w.scale, w.causal)
@@ -823,15 +833,22 @@ def calibrate_mode(reps: int = 5, mfma_seconds: float = 3.0):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline():
-    """The fp64 oracle, as it stands, on a bounded sample of the same workload:
-    head 0 of the 64K causal workload restricted to its first 16384 queries and
-    keys (causal rows 0..16383 see only keys 0..16383, so this is the top-left
-    block of the real problem), forward + Setting 1 + Setting 2 backward."""
+def cpu_baseline(w: W.Workload):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload,
+    forward + Setting 1 + Setting 2 backward on head 0.  Causal: the first
+    (at most) 16384 queries with every key they may see (the top-left block of
+    the real problem; for the 64K causal workload, rows 0..16383 against keys
+    0..16383).  Non-causal: the first (at most) 8192 queries against the first
+    keys, at most 2^25 pairs in all."""
     import oracle
-    w = W.WORKLOADS["causal64k"]
-    n = 16384
-    sub = w.replace(n_q=n, n_k=n, heads=1)
+    if w.causal:
+        m = min(w.n_q, 16384)
+        sub = w.replace(n_q=m, n_k=m + (w.n_k - w.n_q), heads=1)
+        what = f"first {m} queries x {sub.n_k} keys (causal)"
+    else:
+        m = min(w.n_q, 8192)
+        sub = w.replace(n_q=m, n_k=min(w.n_k, (1 << 25) // m), heads=1)
+        what = f"first {m} queries x first {sub.n_k} keys"
     q1, k1, q2, k2 = W.head_inputs(sub, 0)   # prefix rows of head 0's draws
     try:
         from threadpoolctl import threadpool_info
@@ -839,14 +856,14 @@ def cpu_baseline():
     except Exception:
         cores = os.cpu_count() or 1
     t0 = time.perf_counter()
-    oracle.forward_head(q1, k1, q2, k2, w.scale, True)
-    oracle.backward_head(1, q1, k1, q2, k2, w.scale, True)
-    oracle.backward_head(2, q1, k1, q2, k2, w.scale, True)
+    oracle.forward_head(q1, k1, q2, k2, w.scale, w.causal)
+    oracle.backward_head(1, q1, k1, q2, k2, w.scale, w.causal)
+    oracle.backward_head(2, q1, k1, q2, k2, w.scale, w.causal)
     dt = time.perf_counter() - t0
     flop = 20 * w.head_dim * sub.elements()
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "host_cores": os.cpu_count(),
             "kind": "oracle",
-            "sample": f"head 0 of causal64k, first {n} queries x {n} keys (causal), fwd + bwd Setting 1 + "
+            "sample": f"head 0 of {w.name}, {what}, fwd + bwd Setting 1 + "
                       f"Setting 2, fp64 numpy/BLAS; {dt:.1f} s for {flop / 1e12:.3f} TFLOP"}
 
 
@@ -1143,7 +1160,8 @@ def main():
         parts["bwd_set2_ms"] = round(bwd2_ms, 3)
         parts["bwd_set1_tflops"] = round(flop_bwd / (bwd1_ms * 1e-3) / 1e12, 1)
         parts["bwd_set2_tflops"] = round(flop_bwd / (bwd2_ms * 1e-3) / 1e12, 1)
-    parts["pct_mfma_peak_step"] = round(100 * value / PEAK_BF16_TFLOPS, 2)
+    peak = peak_tflops(w.dtype)
+    parts["pct_mfma_peak_step"] = round(100 * value / peak, 2)
     if args.gemm_ref and not args.no_gemm_ref:
         gemm = gemm_reference()
         parts["gemm_bf16_16384_tflops"] = round(gemm, 1)
@@ -1156,12 +1174,14 @@ def main():
     j = int(np.argmax(mean_call))
     kname, kflop = calls[j]
     achieved = kflop * d * E / (mean_call[j] * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": kname, "achieved": round(float(achieved), 1), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(float(achieved) / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic(kname),
+    roofline = {"bound": "mfma", "kernel": kname, "achieved": round(float(achieved), 1), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(float(achieved) / peak, 4),
+                "traffic": measured_traffic(kname, w.name),
                 "avg_launch_ms": round(float(mean_call[j]), 3),
                 "work_per_launch": f"{kflop}*d flop x {E} unmasked pairs = {kflop * d * E / 1e12:.3f} TFLOP"}
-    if not args.no_ceiling:
+    if w.dtype != "bf16":
+        parts["mfma_ceiling"] = {"skipped": "the probes run bf16 MFMAs; this workload is " + w.dtype}
+    elif not args.no_ceiling:
         # each kernel's executed MFMA rate (k*d flop per pair, as it runs)
         # against the probe at its occupancy: the both-settings and fused
         # kernels run one wave per SIMD, the others two
@@ -1175,19 +1195,23 @@ def main():
                 ceil[f"{name}_frac"] = round(k * d * E / (parts[name]["ms"] * 1e-3) / 1e12
                                              / ceil[f"lds_operand_{wps}_wave_per_simd_tflops"], 3)
         parts["mfma_ceiling"] = ceil
+    mask = "causal" if causal else "non-causal"
+    sizes = f"N_Q=N_K={w.n_q}" if w.n_q == w.n_k else f"N_Q={w.n_q}, N_K={w.n_k}"
     out = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "metric": METRIC if w.name == "causal64k" else
+        f"fwd/bwd TFLOP/s + ms, {w.heads} heads d={d} {w.dtype} {mask} {sizes}; % MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": f"{w.name}: {w.heads} heads, N_Q=N_K={w.n_q}, head_dim={d}, bf16, causal, "
-                               "correlated student; step = fwd + bwd Setting 1 + bwd Setting 2",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.heads} heads, {sizes}, head_dim={d}, {w.dtype}, {mask}, "
+                               f"{w.student} student; step = fwd + bwd Setting 1 + bwd Setting 2",
                    "heads": w.heads, "n_q": w.n_q, "n_k": w.n_k, "head_dim": d, "causal": causal,
                    "bwd_path": path},
         "parts": parts,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline()
+        out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
 
 
