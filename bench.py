@@ -833,6 +833,17 @@ def calibrate_mode(reps: int = 5, mfma_seconds: float = 3.0):
     print(json.dumps(out), flush=True)
 
 
+def cpu_sample(w: W.Workload):
+    """The one-head sub-workload the CPU baseline runs, and its description."""
+    if w.causal:
+        m = min(w.n_q, 16384)
+        sub = w.replace(n_q=m, n_k=m + (w.n_k - w.n_q), heads=1)
+        return sub, f"first {m} queries x {sub.n_k} keys (causal)"
+    m = min(w.n_q, 8192)
+    sub = w.replace(n_q=m, n_k=min(w.n_k, (1 << 25) // m), heads=1)
+    return sub, f"first {m} queries x first {sub.n_k} keys"
+
+
 def cpu_baseline(w: W.Workload):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload,
     forward + Setting 1 + Setting 2 backward on head 0.  Causal: the first
@@ -841,14 +852,7 @@ def cpu_baseline(w: W.Workload):
     0..16383).  Non-causal: the first (at most) 8192 queries against the first
     keys, at most 2^25 pairs in all."""
     import oracle
-    if w.causal:
-        m = min(w.n_q, 16384)
-        sub = w.replace(n_q=m, n_k=m + (w.n_k - w.n_q), heads=1)
-        what = f"first {m} queries x {sub.n_k} keys (causal)"
-    else:
-        m = min(w.n_q, 8192)
-        sub = w.replace(n_q=m, n_k=min(w.n_k, (1 << 25) // m), heads=1)
-        what = f"first {m} queries x first {sub.n_k} keys"
+    sub, what = cpu_sample(w)
     q1, k1, q2, k2 = W.head_inputs(sub, 0)   # prefix rows of head 0's draws
     try:
         from threadpoolctl import threadpool_info

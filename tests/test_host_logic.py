@@ -126,6 +126,28 @@ def test_traffic_files_per_workload(tmp_path, monkeypatch):
     assert bench.measured_traffic("bwd_kv_kernel set1", "decode512k") is None
 
 
+def test_bench_peak_and_cpu_sample_follow_the_workload():
+    assert bench.peak_tflops("bf16") == 2516.6 and bench.peak_tflops("fp32") == 157.3
+    for name, w in W.WORKLOADS.items():
+        sub, what = bench.cpu_sample(w)
+        assert sub.heads == 1 and sub.n_q <= w.n_q and sub.n_k <= w.n_k and sub.causal == w.causal
+        assert (sub.dtype, sub.student, sub.seed, sub.head_dim) == (w.dtype, w.student, w.seed, w.head_dim)
+        # bounded: at most 16384 causal rows (1.3e8 pairs) or 2^25 non-causal pairs
+        assert sub.elements() <= max(16384 * 16385 // 2, 1 << 25), name
+        if w.causal:   # the same causal offset: the top-left block of the real mask
+            assert sub.n_k - sub.n_q == w.n_k - w.n_q
+    sub, what = bench.cpu_sample(W.WORKLOADS["causal64k"])
+    assert (sub.n_q, sub.n_k) == (16384, 16384) and what == "first 16384 queries x 16384 keys (causal)"
+    sub, _ = bench.cpu_sample(W.WORKLOADS["smallq128k"])
+    assert (sub.n_q, sub.n_k) == (512, 65536)
+    # prefix rows: the sample's inputs are the first rows of the full workload's head 0
+    w = W.WORKLOADS["causal8k"].replace(n_q=64, n_k=64)
+    full = W.head_inputs(w, 0)
+    part = W.head_inputs(w.replace(n_q=16, n_k=16), 0)
+    for a, b in zip(full, part):
+        assert np.array_equal(a[:16], b)
+
+
 def test_bench_refuses_more_than_one_gpu():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
