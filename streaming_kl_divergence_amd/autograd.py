@@ -12,9 +12,11 @@ P1 does not depend on (Q2, K2) and P2 does not depend on (Q1, K1), so each
 setting's gradients are the true partial derivatives, and "both" (the two
 settings together) is the full gradient of the loss.
 
-Every step runs in the HIP library: the forward kernel, and in the backward
-only the kernels for the gradients autograd asks for (the dK-only or dQ-only
-launch when just one of Q, K needs one).  The library's gradients are fp32;
+Every step runs in the HIP library: the forward (the one-pass kernel, or the
+split-K pair of Methodology 3 when the query blocks alone cannot fill the GPU,
+as the library's split-count heuristic decides), and in the backward only the
+kernels for the gradients autograd asks for (the dK-only or dQ-only launch
+when just one of Q, K needs one).  The library's gradients are fp32;
 they are returned in the inputs' dtype, as autograd requires.
 """
 from __future__ import annotations
@@ -29,7 +31,7 @@ _SETTINGS = ("student", "teacher", "both")
 class _AttentionKL(torch.autograd.Function):
     @staticmethod
     def forward(ctx, q1, k1, q2, k2, scale, causal, setting):
-        kl, lse1, lse2 = ops.fwd(q1, k1, q2, k2, scale, causal)
+        kl, lse1, lse2 = ops.fwd_auto(q1, k1, q2, k2, scale, causal)
         ctx.save_for_backward(q1, k1, q2, k2, kl, lse1, lse2)
         ctx.scale, ctx.causal, ctx.setting = scale, causal, setting
         return kl

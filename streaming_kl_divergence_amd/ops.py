@@ -110,6 +110,17 @@ def splitk_auto(n_q, n_k, heads, head_dim) -> int:
     return _lib.lib().streamkl_splitk_auto(n_q, n_k, heads, head_dim)
 
 
+def fwd_auto(q1, k1, q2, k2, scale: float, causal: bool):
+    """The forward the library recommends for the shape: split-K when its
+    split-count heuristic (streamkl_splitk_auto) asks for more than one key
+    range, which it does when the query blocks alone cannot fill the GPU
+    (short query sets, decode), else the one-pass kernel."""
+    heads, n_q, n_k, d, _ = _inputs(q1, k1, q2, k2)
+    if splitk_auto(n_q, n_k, heads, d) > 1:
+        return fwd_splitk(q1, k1, q2, k2, scale, causal)
+    return fwd(q1, k1, q2, k2, scale, causal)
+
+
 def bwd_select(n_q, n_k, heads, head_dim, causal) -> str:
     return {_lib.BWD_FUSED: "fused", _lib.BWD_SEPARATE: "separate"}[
         _lib.lib().streamkl_bwd_select(n_q, n_k, heads, head_dim, int(causal))]

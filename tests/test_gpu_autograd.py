@@ -65,6 +65,34 @@ def test_attention_kl_autograd(idx):
             assert tt.grad is None, f"{names[i]} should get no gradient in setting {setting}"
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_attention_kl_short_queries_take_split_k(causal):
+    """40 queries against 3000 keys: too few query blocks to fill the GPU, so
+    the forward runs split-K (bitwise what fwd_splitk returns) and the loss and
+    all four gradients still match the oracle."""
+    need_gpu()
+    import torch
+    import streaming_kl_divergence_amd as skl
+    heads, n_q, n_k, d, dtype = 2, 40, 3000, 128, "bf16"
+    log(f"case autograd short queries causal={causal}")
+    assert skl.splitk_auto(n_q, n_k, heads, d) > 1
+    arrs = _rand_case(450 + int(causal), heads, n_q, n_k, d, dtype)
+    g = np.random.default_rng(550).uniform(0.5, 1.5, (heads, n_q)).astype(np.float32)
+    scale = 1 / np.sqrt(d)
+    t = _leaves(arrs, dtype, (True, True, True, True))
+    kl = skl.attention_kl(*t, scale=scale, causal=causal, setting="both")
+    ksp, _, _ = skl.fwd_splitk(*(x.detach() for x in t), scale, causal)
+    assert torch.equal(kl.detach(), ksp)
+    (kl * torch.from_numpy(g).cuda()).sum().backward()
+    torch.cuda.synchronize()
+    rkl, _, _ = oracle.forward(*arrs, scale, causal)
+    compare(kl.detach().cpu().numpy(), rkl, dtype, "kl")
+    ref = dict(zip((2, 3), oracle.backward(1, *arrs, scale, causal, dkl=g)))
+    ref.update(zip((0, 1), oracle.backward(2, *arrs, scale, causal, dkl=g)))
+    for i, name in enumerate(("q1", "k1", "q2", "k2")):
+        compare(t[i].grad.float().cpu().numpy(), ref[i], dtype, f"grad {name}")
+
+
 def test_attention_kl_rejects_unknown_setting():
     import streaming_kl_divergence_amd as skl
     with pytest.raises(ValueError):
