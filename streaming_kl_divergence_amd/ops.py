@@ -114,7 +114,8 @@ def fwd_auto(q1, k1, q2, k2, scale: float, causal: bool):
     """The forward the library recommends for the shape: split-K when its
     split-count heuristic (streamkl_splitk_auto) asks for more than one key
     range, which it does when the query blocks alone cannot fill the GPU
-    (short query sets, decode), else the one-pass kernel."""
+    (short query sets, decode), else the one-pass kernel.  A STREAMKL_SPLITS
+    override is what the heuristic then returns, so it picks the path too."""
     heads, n_q, n_k, d, _ = _inputs(q1, k1, q2, k2)
     if splitk_auto(n_q, n_k, heads, d) > 1:
         return fwd_splitk(q1, k1, q2, k2, scale, causal)
