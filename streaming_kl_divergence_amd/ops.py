@@ -1,7 +1,10 @@
 """Torch-facing wrappers over the C ABI.  Every step runs in the HIP library;
 these functions only check tensors, allocate outputs with torch and pass
-pointers and the current stream."""
+pointers and the current stream of the inputs' device (made current for the
+call)."""
 from __future__ import annotations
+
+import functools
 
 import torch
 
@@ -20,6 +23,8 @@ def _inputs(q1, k1, q2, k2):
             raise ValueError("inputs must be contiguous [heads, n, head_dim]")
         if t.dim() != 3:
             raise ValueError("inputs must be [heads, n, head_dim]")
+    if len({q1.device, k1.device, q2.device, k2.device}) != 1:
+        raise ValueError("inputs must be on one device")
     if len({q1.dtype, k1.dtype, q2.dtype, k2.dtype}) != 1 or q1.dtype not in _DT:
         raise ValueError("inputs must share one dtype: bfloat16 or float32")
     heads, n_q, d = q1.shape
@@ -71,10 +76,24 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
+def _on_device(fn):
+    """Run an entry point with the inputs' device current, so the library
+    launches on that device and on its current stream."""
+    @functools.wraps(fn)
+    def wrapped(*args, **kw):
+        q1 = next((a for a in args if isinstance(a, torch.Tensor)), None)
+        if q1 is None or not q1.is_cuda:
+            return fn(*args, **kw)    # the entry point's own checks reject it
+        with torch.cuda.device(q1.device):
+            return fn(*args, **kw)
+    return wrapped
+
+
 def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+@_on_device
 def fwd(q1, k1, q2, k2, scale: float, causal: bool):
     """Per-row (KL, LSE1, LSE2), fp32 [heads, n_q]."""
     heads, n_q, n_k, d, dt = _inputs(q1, k1, q2, k2)
@@ -89,6 +108,7 @@ def splitk_workspace_bytes(n_q, n_k, heads, head_dim, num_splits=0) -> int:
     return _lib.lib().streamkl_workspace_bytes(0, n_q, n_k, heads, head_dim, num_splits, 0)
 
 
+@_on_device
 def fwd_splitk(q1, k1, q2, k2, scale: float, causal: bool, num_splits: int = 0, workspace=None):
     """Split-K forward; num_splits = 0 lets the library choose."""
     heads, n_q, n_k, d, dt = _inputs(q1, k1, q2, k2)
@@ -110,6 +130,7 @@ def splitk_auto(n_q, n_k, heads, head_dim) -> int:
     return _lib.lib().streamkl_splitk_auto(n_q, n_k, heads, head_dim)
 
 
+@_on_device
 def fwd_auto(q1, k1, q2, k2, scale: float, causal: bool):
     """The forward the library recommends for the shape: split-K when its
     split-count heuristic (streamkl_splitk_auto) asks for more than one key
@@ -127,6 +148,7 @@ def bwd_select(n_q, n_k, heads, head_dim, causal) -> str:
         _lib.lib().streamkl_bwd_select(n_q, n_k, heads, head_dim, int(causal))]
 
 
+@_on_device
 def bwd(setting: int, q1, k1, q2, k2, scale: float, causal: bool, lse1, lse2, kl=None, dkl=None,
         path: str = "auto", dq=None, dk=None):
     """(dQ, dK) of the setting's tensors (Setting 1: Q2, K2; Setting 2: Q1, K1), fp32.
@@ -163,6 +185,7 @@ def bwd(setting: int, q1, k1, q2, k2, scale: float, causal: bool, lse1, lse2, kl
     return dq, dk
 
 
+@_on_device
 def bwd_both(q1, k1, q2, k2, scale: float, causal: bool, lse1, lse2, kl, dkl=None, path: str = "auto", dq1=None,
              dk1=None, dq2=None, dk2=None):
     """(dQ1, dK1, dQ2, dK2), fp32: Setting 2's and Setting 1's gradients of the
